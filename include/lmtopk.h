@@ -1,0 +1,210 @@
+/*
+ * lmtopk.h - C ABI of liblmtopk: the LM-head (vocabulary) projection fused with
+ * exact top-k selection, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (lm-head-topk page, intro and section "Method"): for every
+ * decode row m the library forms the logits L[m, v] of all V vocabulary entries
+ * and returns only the k largest, as (values [M,k] fp32, indices [M,k] int64)
+ * sorted by value descending; equal values are ordered by the lower vocabulary
+ * index first (section "Method", last sentence; section "API").  The full logit
+ * vector is never written to device memory: each chunk of the vocabulary is
+ * scored on chip and offers its own exact top-k, and a merge pass reduces the
+ * chunk candidates (section "Method").
+ *
+ * Conventions shared by every entry point
+ *  - All array arguments are DEVICE pointers unless stated otherwise; `stream`
+ *    is a hipStream_t passed as void* (NULL = the null stream).
+ *  - Every call is asynchronous on `stream`.  The library allocates and frees
+ *    no memory; the caller owns every buffer, including outputs and workspace.
+ *    Inputs are read only; outputs are fully overwritten on success.
+ *  - Arrays are dense and row-major.  Every pointer must be 16-byte aligned.
+ *  - Arguments are checked on the host BEFORE anything is enqueued.  On any
+ *    error status nothing is launched and nothing is written.  A failure
+ *    reported by the HIP runtime while enqueueing maps to LMTOPK_ERR_HIP; a
+ *    fault inside a kernel surfaces at the caller's next synchronisation, as
+ *    for any asynchronous HIP work.
+ *  - The library is stateless and thread safe.  Calls that share a workspace
+ *    buffer must be ordered on one stream.
+ *  - Inputs must be finite or +-inf.  NaN anywhere is outside the contract and
+ *    gives an unspecified (but memory-safe) result.
+ *  - +0.0 and -0.0 compare equal: they tie and the lower index comes first.
+ *    A returned value keeps the bits of that index's own logit.
+ *
+ * Limits (lm-head-topk page, section "Requirements and limits"): 1 <= k <=
+ * min(V, 2048).  Rows per call: 1 <= M <= 8 (the page tests 1 to 8 rows in its
+ * section "Correctness"); every weight byte is read once per call for all M
+ * rows.  V < 2^31.
+ */
+#ifndef LMTOPK_H
+#define LMTOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Status codes                                                              */
+/* ------------------------------------------------------------------------ */
+typedef enum {
+  LMTOPK_OK = 0,
+  LMTOPK_ERR_NULL = 1,      /* a required pointer is NULL                     */
+  LMTOPK_ERR_SHAPE = 2,     /* M not in [1,8], V < 1, V >= 2^31, H < 1, ld < V,
+                               or a size limit below is exceeded              */
+  LMTOPK_ERR_K = 3,         /* k < 1 or k > min(V, 2048)                      */
+  LMTOPK_ERR_GROUP = 4,     /* group_size != 128 or H % 128 != 0 (binary)     */
+  LMTOPK_ERR_DTYPE = 5,     /* unknown lmtopk_dtype                           */
+  LMTOPK_ERR_ALIGN = 6,     /* a pointer is not 16-byte aligned, or a dense
+                               row is not a whole number of 16-byte vectors   */
+  LMTOPK_ERR_WORKSPACE = 7, /* workspace NULL or smaller than required        */
+  LMTOPK_ERR_OPTIONS = 8,   /* invalid lmtopk_options field                  */
+  LMTOPK_ERR_HIP = 9        /* the HIP runtime refused a launch               */
+} lmtopk_status;
+
+typedef enum { LMTOPK_F32 = 0, LMTOPK_BF16 = 1 } lmtopk_dtype;
+
+/* Optional per-call settings; pass NULL for the defaults. */
+typedef struct {
+  /* Vocabulary rows per chunk (one workgroup scores and selects one chunk).
+     0 = automatic.  Otherwise a multiple of 64 that is <= 1024, or one of
+     2048 and 4096.  The result never depends on this value. */
+  int32_t chunk_rows;
+  int32_t reserved; /* must be 0 */
+  /* If not NULL: a hipEvent_t (as void*) that is recorded on `stream` right
+     after the chunk-scoring kernel is enqueued, so a caller can time the
+     scoring kernel apart from the merge.  The library does not own it. */
+  void* score_event;
+} lmtopk_options;
+
+/* ------------------------------------------------------------------------ */
+/* Packed binary head, layout version 1                                      */
+/* ------------------------------------------------------------------------ */
+/*
+ * A binary head stores each weight as a sign (+1 or -1) and each group of 128
+ * consecutive weights of one vocabulary row as one fp32 scale, so that the
+ * dequantized weight is sign * scale (lm-head-topk page, section "Usage" for
+ * the argument list and group_size=128; section "Requirements and limits" for
+ * packing as a separate offline step).  The pages do not give the packed
+ * layout; this library defines its own:
+ *
+ *   G   = H / 128             groups per vocabulary row
+ *   G4  = ceil(G / 4) * 4     groups rounded up to whole quads
+ *   V64 = ceil(V / 64) * 64   vocabulary rows rounded up to whole 64-row tiles
+ *   row v lives in tile t = v / 64 at lane r = v % 64
+ *
+ *   wq     : uint32 words, word index ((t * G + g) * 64 + r) * 4 + w for
+ *            g < G, w < 4.  Bit b (value 1 << b) of that word is the sign of
+ *            element j = 128 * g + 32 * w + b of row v: 1 means +1 (the
+ *            source weight was >= 0, so -0.0 packs as +1), 0 means -1.
+ *            Size V64 * H / 8 bytes.
+ *   wscale : fp32, index ((t * (G4 / 4) + q) * 64 + r) * 4 + i holds the
+ *            scale of group g = 4 * q + i of row v.  Size V64 * G4 * 4 bytes.
+ *
+ *   Rows v >= V and groups g >= G are padding: their sign words and scales
+ *   are 0.  The scoring kernels never offer padding rows as candidates.
+ *
+ * One 64-lane wavefront reading one uint4 per lane (one group of one row per
+ * lane) thus reads 1 KiB of contiguous memory, and one float4 per lane reads
+ * the scales of four consecutive groups.
+ */
+#define LMTOPK_LAYOUT_VERSION 1
+#define LMTOPK_GROUP_SIZE 128
+#define LMTOPK_MAX_ROWS 8
+#define LMTOPK_MAX_K 2048
+/* Binary path: the per-row activation bit planes live in LDS, M * H bytes. */
+#define LMTOPK_MAX_BINARY_MH 65536
+
+/* Layout version of packed heads this library reads and writes. */
+int32_t lmtopk_layout_version(void);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* lmtopk_status_string(lmtopk_status s);
+
+/* Host-only: byte sizes of the two packed arrays for a V x H head.
+   Errors: NULL (an out pointer), SHAPE (V < 1, V >= 2^31, H < 1),
+   GROUP (group_size != 128 or H % 128 != 0). */
+lmtopk_status lmtopk_packed_bytes(int64_t V, int64_t H, int32_t group_size,
+                                  size_t* wq_bytes, size_t* wscale_bytes);
+
+/* Host-only: workspace bytes needed by lmtopk_binary, lmtopk_dense and
+   lmtopk_select for these sizes and options.  The same workspace serves all
+   three.  Errors: NULL, SHAPE, K, OPTIONS. */
+lmtopk_status lmtopk_workspace_bytes(int64_t M, int64_t V, int32_t k,
+                                     const lmtopk_options* opt, size_t* bytes);
+
+/*
+ * Pack a dense head into the layout above (offline; once per model).
+ *   w      : [V, H] row-major, fp32 or bf16 (w_dtype).
+ *   wq     : out, lmtopk_packed_bytes(...).wq_bytes bytes.
+ *   wscale : out, lmtopk_packed_bytes(...).wscale_bytes bytes.
+ * Sign: +1 iff w >= 0.  Scale of a group: the mean of |w| over its 128
+ * elements, summed in fp64 and rounded once to fp32.
+ * Errors: NULL, SHAPE, GROUP, DTYPE, ALIGN, HIP.
+ */
+lmtopk_status lmtopk_pack_binary(const void* w, lmtopk_dtype w_dtype, int64_t V,
+                                 int64_t H, int32_t group_size, void* wq,
+                                 float* wscale, void* stream);
+
+/*
+ * Binary head: logits, then exact top-k (lm-head-topk page, section "Usage",
+ * binary entry point; section "Correctness" for what it must match).
+ *   act_q     : [M, H] int8 activations (the full int8 range is accepted).
+ *   act_scale : [M] fp32 per-row activation scale.
+ *   wq, wscale: packed head (layout above) of V rows and H columns.
+ *   bias      : [V] fp32 or NULL.
+ *   values    : out [M, k] fp32;  indices : out [M, k] int64.
+ *   workspace : lmtopk_workspace_bytes(M, V, k, opt) bytes, device.
+ * Logit of row m, entry v:
+ *   D_g = sum over the 128 j of group g of act_q[m, j] * sign[v, j]  (exact)
+ *   acc = fp32 fused multiply-add chain over g = 0, 1, ..., G-1 of
+ *         (float)D_g * wscale[v, g], starting from 0
+ *   L   = fmaf(acc, act_scale[m], bias ? bias[v] : 0)
+ * Errors: NULL, SHAPE (also M * H > LMTOPK_MAX_BINARY_MH), K, GROUP, ALIGN,
+ * WORKSPACE, OPTIONS, HIP.
+ */
+lmtopk_status lmtopk_binary(const int8_t* act_q, const float* act_scale,
+                            const void* wq, const float* wscale,
+                            const float* bias, int64_t M, int64_t V, int64_t H,
+                            int32_t group_size, int32_t k, float* values,
+                            int64_t* indices, void* workspace,
+                            size_t workspace_bytes, const lmtopk_options* opt,
+                            void* stream);
+
+/*
+ * Dense head: logits, then exact top-k (lm-head-topk page, section "Usage",
+ * dense entry point, which the page keeps as the correctness reference).
+ *   hidden : [M, H], weight : [V, H]; both fp32 or both bf16 (dtype).
+ *   bias   : [V] fp32 or NULL.
+ * L[m, v] = sum_j hidden[m, j] * weight[v, j] accumulated in fp32 (products of
+ * bf16 inputs are exact in fp32) in one fixed order that is the same for every
+ * (m, v), then + bias[v].
+ * H * element size must be a multiple of 16 bytes (ALIGN otherwise).
+ * Errors: NULL, SHAPE, K, DTYPE, ALIGN, WORKSPACE, OPTIONS, HIP.
+ */
+lmtopk_status lmtopk_dense(const void* hidden, const void* weight,
+                           lmtopk_dtype dtype, const float* bias, int64_t M,
+                           int64_t V, int64_t H, int32_t k, float* values,
+                           int64_t* indices, void* workspace,
+                           size_t workspace_bytes, const lmtopk_options* opt,
+                           void* stream);
+
+/*
+ * Selection stage alone on logits already in device memory: the exact top-k
+ * of logits[m, 0:V] for each row (row stride ld >= V elements).  Same chunked
+ * select and merge kernels as the fused paths, so the chunk select and merge
+ * can be checked bit for bit against a plain sort.
+ * Errors: NULL, SHAPE, K, ALIGN, WORKSPACE, OPTIONS, HIP.
+ */
+lmtopk_status lmtopk_select(const float* logits, int64_t M, int64_t V,
+                            int64_t ld, int32_t k, float* values,
+                            int64_t* indices, void* workspace,
+                            size_t workspace_bytes, const lmtopk_options* opt,
+                            void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMTOPK_H */

@@ -1,0 +1,50 @@
+"""CPU oracle for the fused LM-head projection + exact top-k.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this package:
+only the tests, the smoke check and the benchmark's CPU-baseline leg do.  It
+shares no code with the HIP library or its Python binding.
+
+What it is: the plain definition of what the method computes, written out in
+NumPy float64 (lm-head-topk page, intro and section "Method"): form every
+logit of the vocabulary projection, then take the k largest under the total
+order (value descending, lower vocabulary index first on ties) with a stable
+sort.  No chunking, no selection algorithm, no fusion: the method's chunked
+select-and-merge reaches exactly this result, so the definition is the oracle.
+
+Modules
+  projection  -- dense and binary (dequantized) projection in float64, bf16
+                 widening.
+  select      -- stable top-k and a sort-free certificate of a top-k result.
+  packing     -- logical sign/scale packing of a dense head, and this
+                 library's packed byte layout (version 1) written and read by
+                 the oracle's own code from the layout's specification.
+"""
+
+from .projection import (
+    bf16_bits_to_f32,
+    dequantize_binary,
+    project_binary,
+    project_dense,
+)
+from .select import certify_topk, float_key_order, topk_stable, topk_stable_rows
+from .packing import (
+    pack_layout_bytes,
+    pack_logical,
+    packed_sizes,
+    unpack_layout_bytes,
+)
+
+__all__ = [
+    "bf16_bits_to_f32",
+    "dequantize_binary",
+    "project_binary",
+    "project_dense",
+    "certify_topk",
+    "float_key_order",
+    "topk_stable",
+    "topk_stable_rows",
+    "pack_layout_bytes",
+    "pack_logical",
+    "packed_sizes",
+    "unpack_layout_bytes",
+]

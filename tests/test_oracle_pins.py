@@ -1,0 +1,331 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each check targets a plausible mistake: a wrong tie rule or sign of zero in
+the selection, a transposed operand, a dropped bias, a wrong group index or
+scale in the binary projection, a wrong bit order or padding in the layout.
+"""
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# selection
+# --------------------------------------------------------------------------
+def rank_by_counting(row):
+    """rank(i) = #{j : x_j > x_i, or x_j == x_i and j < i} (pure Python)."""
+    n = len(row)
+    ranks = []
+    for i in range(n):
+        r = 0
+        for j in range(n):
+            if row[j] > row[i] or (row[j] == row[i] and j < i):
+                r += 1
+        ranks.append(r)
+    return ranks
+
+
+def test_topk_brute_force_all_small_patterns():
+    """Every pattern over {-1, -0.0, +0.0, 1, 2}^V for V <= 5 and every k."""
+    alphabet = [-1.0, -0.0, 0.0, 1.0, 2.0]
+    for V in range(1, 6):
+        for pattern in itertools.product(alphabet, repeat=V):
+            row = np.array(pattern, dtype=np.float32)
+            ranks = rank_by_counting(list(pattern))
+            by_rank = [None] * V
+            for i, r in enumerate(ranks):
+                by_rank[r] = i
+            for k in range(1, V + 1):
+                vals, idx = oracle.topk_stable(row, k)
+                assert list(idx) == by_rank[:k], (pattern, k)
+                assert np.array_equal(vals.view(np.uint32), row[by_rank[:k]].view(np.uint32))
+
+
+def test_topk_brute_force_random_with_ties():
+    rng = np.random.default_rng(123)
+    for trial in range(200):
+        V = int(rng.integers(1, 40))
+        row = rng.integers(-3, 4, size=V).astype(np.float64) * 0.5
+        ranks = rank_by_counting(list(row))
+        by_rank = sorted(range(V), key=lambda i: ranks[i])
+        k = int(rng.integers(1, V + 1))
+        _, idx = oracle.topk_stable(row, k)
+        assert list(idx) == by_rank[:k]
+
+
+def test_topk_golden_hand_worked():
+    with open(os.path.join(GOLDEN, "topk_tiny.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        row = np.array([float(s) for s in case["row"]], dtype=np.float32)
+        vals, idx = oracle.topk_stable(row, case["k"])
+        assert list(idx) == case["indices"]
+        # the value returned is that index's own bits (-0.0 stays -0.0)
+        assert np.array_equal(vals.view(np.uint32), row[idx].view(np.uint32))
+
+
+def test_k1_is_first_argmax():
+    rng = np.random.default_rng(5)
+    for _ in range(100):
+        row = rng.integers(0, 5, size=int(rng.integers(1, 100))).astype(np.float32)
+        _, idx = oracle.topk_stable(row, 1)
+        assert idx[0] == int(np.argmax(row))  # np.argmax returns the first maximum
+
+
+def test_all_equal_gives_first_k():
+    row = np.full(1000, 0.25, dtype=np.float32)
+    _, idx = oracle.topk_stable(row, 37)
+    assert list(idx) == list(range(37))
+
+
+def test_certificate_accepts_and_rejects():
+    rng = np.random.default_rng(9)
+    row = rng.integers(-5, 5, size=300).astype(np.float32)
+    k = 40
+    vals, idx = oracle.topk_stable(row, k)
+    assert oracle.certify_topk(row, vals, idx, k)[0]
+    # swapped pair
+    i2 = idx.copy(); i2[[3, 4]] = i2[[4, 3]]
+    assert not oracle.certify_topk(row, row[i2], i2, k)[0]
+    # a left-out entry that beats the k-th
+    i3 = idx.copy(); i3[-1] = int(np.argmin(row))
+    assert not oracle.certify_topk(row, row[i3], i3, k)[0]
+    # tie broken toward the higher index
+    row4 = np.zeros(10, dtype=np.float32)
+    assert not oracle.certify_topk(row4, row4[[1]], np.array([1]), 1)[0]
+    assert oracle.certify_topk(row4, row4[[0]], np.array([0]), 1)[0]
+    # wrong bits for a value (-0.0 reported as +0.0)
+    row5 = np.array([-0.0, -1.0], dtype=np.float32)
+    assert oracle.certify_topk(row5, np.array([-0.0], np.float32), np.array([0]), 1)[0]
+    assert not oracle.certify_topk(row5, np.array([0.0], np.float32), np.array([0]), 1)[0]
+
+
+# --------------------------------------------------------------------------
+# dense projection
+# --------------------------------------------------------------------------
+def test_dense_integer_exact_and_non_square():
+    """Small-integer inputs make float64 exact; compare with Python integers."""
+    rng = np.random.default_rng(1)
+    M, H, V = 3, 7, 11
+    h = rng.integers(-9, 10, size=(M, H))
+    w = rng.integers(-9, 10, size=(V, H))
+    b = rng.integers(-9, 10, size=V)
+    L = oracle.project_dense(h.astype(np.float32), w.astype(np.float32), b.astype(np.float32))
+    assert L.shape == (M, V)
+    for m in range(M):
+        for v in range(V):
+            exact = sum(int(h[m, j]) * int(w[v, j]) for j in range(H)) + int(b[v])
+            assert L[m, v] == exact
+
+
+def test_dense_one_hot_and_rank_one():
+    rng = np.random.default_rng(2)
+    V, H = 13, 16
+    w = rng.standard_normal((V, H)).astype(np.float32)
+    bias = rng.standard_normal(V).astype(np.float32)
+    for j in (0, 5, H - 1):
+        h = np.zeros((1, H), dtype=np.float32); h[0, j] = 1.0
+        L = oracle.project_dense(h, w, bias)
+        assert np.array_equal(L[0], w[:, j].astype(np.float64) + bias.astype(np.float64))
+    # rank one: W[v, j] = u_v * z_j  =>  L[m, v] = u_v * (h_m . z), powers of two keep it exact
+    u = 2.0 ** rng.integers(-3, 4, size=V)
+    z = 2.0 ** rng.integers(-3, 4, size=H)
+    W = np.outer(u, z).astype(np.float32)
+    h = (2.0 ** rng.integers(-3, 4, size=(2, H))).astype(np.float32)
+    L = oracle.project_dense(h, W)
+    for m in range(2):
+        hz = sum(Fraction(float(h[m, j])) * Fraction(float(z[j])) for j in range(H))
+        for v in range(V):
+            assert Fraction(L[m, v]) == Fraction(float(u[v])) * hz
+
+
+def test_bf16_widening():
+    bits = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x7F80, 0x4049, 0x0001], dtype=np.uint16)
+    f = oracle.bf16_bits_to_f32(bits)
+    assert f[0] == 1.0 and f[1] == -1.0 and f[2] == 0.0 and np.signbit(f[3]) and f[3] == 0.0
+    assert np.isinf(f[4])
+    assert f[5] == np.float32(3.140625)          # 0x4049 = 1.5703125 * 2
+    assert f[6] == np.float32(2.0 ** -133)       # smallest bf16 subnormal
+
+
+# --------------------------------------------------------------------------
+# binary projection
+# --------------------------------------------------------------------------
+def _tiny_binary(rng, M, V, H):
+    act_q = rng.integers(-128, 128, size=(M, H)).astype(np.int8)
+    act_scale = (rng.random(M).astype(np.float32) + np.float32(0.01))
+    signs = np.where(rng.random((V, H)) < 0.5, 1, -1).astype(np.int8)
+    scales = rng.random((V, H // 128)).astype(np.float32)
+    bias = rng.standard_normal(V).astype(np.float32)
+    return act_q, act_scale, signs, scales, bias
+
+
+def test_binary_one_hot_hits_the_right_group():
+    """act_q = a * e_j: L_v = act_scale * a * sign[v, j] * scale[v, j // 128] + bias_v."""
+    rng = np.random.default_rng(3)
+    V, H = 9, 512
+    _, _, signs, scales, bias = _tiny_binary(rng, 1, V, H)
+    for j, a in ((0, 127), (127, -128), (128, 5), (300, -77), (511, 1)):
+        act_q = np.zeros((1, H), dtype=np.int8); act_q[0, j] = a
+        act_scale = np.array([0.375], dtype=np.float32)
+        L = oracle.project_binary(act_q, act_scale, signs, scales, bias)
+        for v in range(V):
+            expect = (Fraction(0.375) * a * int(signs[v, j]) * Fraction(float(scales[v, j // 128]))
+                      + Fraction(float(bias[v])))
+            assert abs(Fraction(L[0, v]) - expect) <= abs(expect) * Fraction(1, 2 ** 50)
+
+
+def test_binary_exact_rationals():
+    """float64 result within 2^-45 relative of the exact rational value."""
+    rng = np.random.default_rng(4)
+    M, V, H = 2, 5, 256
+    act_q, act_scale, signs, scales, bias = _tiny_binary(rng, M, V, H)
+    L = oracle.project_binary(act_q, act_scale, signs, scales, bias)
+    for m in range(M):
+        for v in range(V):
+            acc = Fraction(0)
+            for j in range(H):
+                acc += int(act_q[m, j]) * int(signs[v, j]) * Fraction(float(scales[v, j // 128]))
+            exact = acc * Fraction(float(act_scale[m])) + Fraction(float(bias[v]))
+            mag = sum(abs(int(act_q[m, j])) * Fraction(float(scales[v, j // 128])) for j in range(H))
+            tol = (mag * Fraction(float(act_scale[m])) + abs(Fraction(float(bias[v])))) * Fraction(1, 2 ** 45)
+            assert abs(Fraction(L[m, v]) - exact) <= tol
+
+
+def test_binary_closed_forms_and_symmetry():
+    rng = np.random.default_rng(6)
+    V, H = 4, 384
+    scales = rng.random((V, 3)).astype(np.float32)
+    # all +1 signs and a constant activation a: L = act_scale * a * 128 * sum_g scale_g
+    signs = np.ones((V, H), dtype=np.int8)
+    act_q = np.full((1, H), 3, dtype=np.int8)
+    L = oracle.project_binary(act_q, np.array([0.5], np.float32), signs, scales)
+    for v in range(V):
+        expect = 0.5 * 3 * 128 * sum(float(s) for s in scales[v])
+        assert math.isclose(L[0, v], expect, rel_tol=1e-14)
+    # flipping every sign negates the bias-free logit exactly
+    act_q, act_scale, signs, scales, _ = _tiny_binary(rng, 2, V, H)
+    L1 = oracle.project_binary(act_q, act_scale, signs, scales)
+    L2 = oracle.project_binary(act_q, act_scale, (-signs).astype(np.int8), scales)
+    assert np.array_equal(L1, -L2)
+    # bias enters once, additively
+    bias = rng.standard_normal(V).astype(np.float32)
+    L3 = oracle.project_binary(act_q, act_scale, signs, scales, bias)
+    assert np.allclose(L3 - L1, bias.astype(np.float64)[None, :], rtol=0, atol=1e-12)
+
+
+def test_binary_equals_dense_on_dequantized_weights():
+    """The binary projection is the dense one on x = act_q*act_scale, W = sign*scale."""
+    rng = np.random.default_rng(7)
+    M, V, H = 3, 17, 256
+    act_q, act_scale, signs, scales, bias = _tiny_binary(rng, M, V, H)
+    x = act_q.astype(np.float64) * act_scale.astype(np.float64)[:, None]
+    W = np.empty((V, H))
+    for v in range(V):
+        for j in range(H):
+            W[v, j] = float(signs[v, j]) * float(scales[v, j // 128])
+    Lb = oracle.project_binary(act_q, act_scale, signs, scales, bias)
+    Ld = oracle.project_dense(x, W, bias)
+    assert np.allclose(Lb, Ld, rtol=1e-13, atol=0)
+
+
+# --------------------------------------------------------------------------
+# packing and layout
+# --------------------------------------------------------------------------
+def test_pack_recovers_known_signs_and_scales():
+    rng = np.random.default_rng(8)
+    V, H = 70, 384
+    signs = np.where(rng.random((V, H)) < 0.5, 1, -1).astype(np.int8)
+    scales = rng.random((V, H // 128)).astype(np.float32) + np.float32(0.5)
+    W = (signs.astype(np.float32) * np.repeat(scales, 128, axis=1)).astype(np.float32)
+    s2, sc2 = oracle.pack_logical(W)
+    assert np.array_equal(s2, signs)
+    assert np.array_equal(sc2.view(np.uint32), scales.view(np.uint32))  # 128 equal values: exact mean
+
+
+def test_pack_zero_sign_and_mean():
+    W = np.zeros((2, 128), dtype=np.float32)
+    W[0, :] = -0.0
+    W[1, :] = np.arange(1, 129, dtype=np.float32)
+    W[1, 0] = -1.0
+    s, sc = oracle.pack_logical(W)
+    assert np.all(s[0] == 1)                   # -0.0 >= 0 packs as +1
+    assert s[1, 0] == -1 and np.all(s[1, 1:] == 1)
+    assert sc[0, 0] == 0.0 and sc[1, 0] == np.float32(64.5)   # mean of 1..128
+
+
+def _golden_head(g):
+    V, H = g["V"], g["H"]
+    W = np.full((V, H), -1.0, dtype=np.float32)
+    j = np.arange(H)
+    W[0] = 1.0
+    W[1] = np.where(j % 2 == 0, 2.0, -2.0)
+    W[63] = np.where(j < 32, 0.5, -0.5)
+    W[64] = np.where(j < 128, -0.0, -3.0)
+    W[64, 165] = 3.0
+    return W
+
+
+def test_layout_golden_hand_derived():
+    with open(os.path.join(GOLDEN, "layout_v1_tiny.json")) as f:
+        g = json.load(f)
+    W = _golden_head(g)
+    signs, scales = oracle.pack_logical(W)
+    wq, ws = oracle.pack_layout_bytes(signs, scales)
+    assert wq.shape == (g["total_words"],) and ws.shape == (g["total_scales"],)
+    wq_b, ws_b = oracle.packed_sizes(g["V"], g["H"])
+    assert wq_b == 4 * g["total_words"] and ws_b == 4 * g["total_scales"]
+    expect = np.zeros_like(wq)
+    for k, v in g["expected_words"].items():
+        expect[int(k)] = int(v, 16)
+    assert np.array_equal(wq, expect)
+    expect_s = np.zeros_like(ws)
+    for r in range(2, 63):
+        expect_s[4 * r] = 1.0
+        expect_s[4 * r + 1] = 1.0
+    for k, v in g["expected_scales"].items():
+        expect_s[int(k)] = v
+    assert np.array_equal(ws, expect_s)
+    # the reader inverts the writer
+    s2, sc2 = oracle.unpack_layout_bytes(wq, ws, g["V"], g["H"])
+    assert np.array_equal(s2, signs) and np.array_equal(sc2, scales)
+
+
+def test_layout_round_trip_random_ragged():
+    rng = np.random.default_rng(10)
+    for V, H in ((1, 128), (63, 128), (65, 640), (130, 256)):
+        signs = np.where(rng.random((V, H)) < 0.5, 1, -1).astype(np.int8)
+        scales = rng.random((V, H // 128)).astype(np.float32)
+        wq, ws = oracle.pack_layout_bytes(signs, scales)
+        wqb, wsb = oracle.packed_sizes(V, H)
+        assert wq.nbytes == wqb and ws.nbytes == wsb
+        s2, sc2 = oracle.unpack_layout_bytes(wq, ws, V, H)
+        assert np.array_equal(s2, signs) and np.array_equal(sc2, scales)
+
+
+# --------------------------------------------------------------------------
+# input generators (not the method, but both sides depend on them)
+# --------------------------------------------------------------------------
+def test_generators_deterministic_and_thread_independent():
+    a = synthetic.normal_rows(20000, 8, seed=3, stream=1, threads=1)
+    b = synthetic.normal_rows(20000, 8, seed=3, stream=1, threads=4)
+    assert np.array_equal(a, b)
+    q, s = synthetic.quantize_rows_int8(np.array([[0.0, 1.5, -2.0, 0.25]], np.float32))
+    assert s[0] == np.float32(2.0 / 127.0)
+    assert list(q[0]) == [0, 95, -127, 16]  # 95.25 -> 95, 15.875 -> 16
+    q0, s0 = synthetic.quantize_rows_int8(np.zeros((1, 4), np.float32))
+    assert s0[0] == 1.0 and not q0.any()
+    bits = synthetic.f32_to_bf16_bits(np.array([1.0, 1.00390625, 1.01171875, -2.5], np.float32))
+    # 1 + 2^-8 is halfway between bf16 neighbours 1 and 1 + 2^-7: ties to even -> 1.0
+    assert list(bits) == [0x3F80, 0x3F80, 0x3F82, 0xC020]
