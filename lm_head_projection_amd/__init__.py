@@ -1,0 +1,264 @@
+"""Python binding of liblmtopk: the LM-head projection fused with exact top-k on MI355X.
+
+Argument marshalling only: tensors are checked and their device pointers,
+sizes and the current HIP stream are handed to the C ABI declared in
+include/lmtopk.h; every step of the computation runs in the library's HIP
+kernels.  PyTorch supplies device memory and streams.
+
+Entry points mirror the lm-head-topk page (section "Usage"):
+    lm_head_topk_binary(act_q, act_scale, wq, wscale, bias=None, group_size=128, k=50, ...)
+    lm_head_topk_dense(hidden, weight, k=50, bias=None, ...)
+plus pack_binary (offline packing of a dense head) and topk_logits (the
+selection stage alone, on logits already in memory).  Each returns
+(values [M, k] float32, indices [M, k] int64), sorted by value descending,
+ties to the lower vocabulary index.
+
+Importing this module raises ImportError if the built library is missing:
+there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LmTopkError",
+    "layout_version",
+    "packed_bytes",
+    "workspace_bytes",
+    "pack_binary",
+    "lm_head_topk_binary",
+    "lm_head_topk_dense",
+    "topk_logits",
+    "library_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_lib", "liblmtopk.so")
+
+GROUP_SIZE = 128
+MAX_ROWS = 8
+MAX_K = 2048
+_F32, _BF16 = 0, 1
+
+
+class LmTopkError(ValueError):
+    """A status other than LMTOPK_OK returned by the library."""
+
+    def __init__(self, status, text):
+        super().__init__(f"liblmtopk status {status}: {text}")
+        self.status = status
+
+
+class _Options(ctypes.Structure):
+    _fields_ = [("chunk_rows", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("score_event", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"liblmtopk is not built ({_LIB_PATH} missing); run "
+            "`python -m lm_head_projection_amd.build` (needs hipcc for gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    psz = ctypes.POINTER(ctypes.c_size_t)
+    popt = ctypes.POINTER(_Options)
+    sig = {
+        "lmtopk_layout_version": ([], i32),
+        "lmtopk_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "lmtopk_packed_bytes": ([i64, i64, i32, psz, psz], ctypes.c_int),
+        "lmtopk_workspace_bytes": ([i64, i64, i32, popt, psz], ctypes.c_int),
+        "lmtopk_pack_binary": ([vp, ctypes.c_int, i64, i64, i32, vp, vp, vp], ctypes.c_int),
+        "lmtopk_binary": ([vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp, sz, popt, vp],
+                          ctypes.c_int),
+        "lmtopk_dense": ([vp, vp, ctypes.c_int, vp, i64, i64, i64, i32, vp, vp, vp, sz, popt, vp],
+                         ctypes.c_int),
+        "lmtopk_select": ([vp, i64, i64, i64, i32, vp, vp, vp, sz, popt, vp], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _check(status):
+    if status != 0:
+        raise LmTopkError(status, _lib.lmtopk_status_string(status).decode())
+
+
+def layout_version():
+    return int(_lib.lmtopk_layout_version())
+
+
+def packed_bytes(V, H, group_size=GROUP_SIZE):
+    """(wq_bytes, wscale_bytes) of a packed V x H head."""
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(_lib.lmtopk_packed_bytes(V, H, group_size, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def _opts(chunk_rows, score_event=None):
+    return _Options(int(chunk_rows), 0, score_event)
+
+
+def workspace_bytes(M, V, k, chunk_rows=0):
+    n = ctypes.c_size_t()
+    o = _opts(chunk_rows)
+    _check(_lib.lmtopk_workspace_bytes(M, V, k, ctypes.byref(o), ctypes.byref(n)))
+    return n.value
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need_cuda(name, t, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _outputs(dev, M, k, out):
+    if out is None:
+        return (torch.empty((M, k), dtype=torch.float32, device=dev),
+                torch.empty((M, k), dtype=torch.int64, device=dev))
+    values, indices = out
+    _need_cuda("values", values, torch.float32, 2)
+    _need_cuda("indices", indices, torch.int64, 2)
+    if tuple(values.shape) != (M, k) or tuple(indices.shape) != (M, k):
+        raise ValueError("out tensors must be [M, k]")
+    return values, indices
+
+
+def _workspace(dev, M, V, k, chunk_rows, workspace):
+    need = workspace_bytes(M, V, k, chunk_rows)
+    if workspace is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need_cuda("workspace", workspace, torch.uint8)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace needs {need} bytes, got {workspace.numel()}")
+    return workspace
+
+
+def pack_binary(weight, group_size=GROUP_SIZE):
+    """Pack a dense head [V, H] (fp32 or bf16) into (wq, wscale), layout version 1.
+
+    wq: uint8 [V64/64, G, 64, 16] sign bits; wscale: float32 [V64/64, G4/4, 64, 4].
+    """
+    _need_cuda("weight", weight, ndim=2)
+    if weight.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("weight must be float32 or bfloat16")
+    V, H = weight.shape
+    wq_b, ws_b = packed_bytes(V, H, group_size)
+    T = -(-V // 64)
+    G = H // group_size
+    Q = -(-G // 4)
+    wq = torch.empty((T, G, 64, 16), dtype=torch.uint8, device=weight.device)
+    ws = torch.empty((T, Q, 64, 4), dtype=torch.float32, device=weight.device)
+    assert wq.numel() == wq_b and ws.numel() * 4 == ws_b
+    dt = _BF16 if weight.dtype == torch.bfloat16 else _F32
+    _check(_lib.lmtopk_pack_binary(_ptr(weight), dt, V, H, group_size, _ptr(wq), _ptr(ws),
+                                   _stream(weight)))
+    return wq, ws
+
+
+def lm_head_topk_binary(act_q, act_scale, wq, wscale, bias=None, group_size=GROUP_SIZE, k=50, *,
+                        vocab_size=None, chunk_rows=0, out=None, workspace=None,
+                        score_event=None):
+    """Exact top-k of the binary-head logits of each activation row.
+
+    act_q int8 [M, H]; act_scale float32 [M]; (wq, wscale) from pack_binary;
+    bias float32 [V] or None.  vocab_size V is required when bias is None
+    (the packed arrays are padded to whole 64-row tiles).
+    """
+    _need_cuda("act_q", act_q, torch.int8, 2)
+    _need_cuda("act_scale", act_scale, torch.float32, 1)
+    _need_cuda("wq", wq)
+    _need_cuda("wscale", wscale, torch.float32)
+    M, H = act_q.shape
+    if act_scale.numel() != M:
+        raise ValueError("act_scale must have M entries")
+    if bias is not None:
+        _need_cuda("bias", bias, torch.float32, 1)
+        V = bias.numel() if vocab_size is None else int(vocab_size)
+        if bias.numel() != V:
+            raise ValueError("bias must have V entries")
+    elif vocab_size is None:
+        raise ValueError("vocab_size is required when bias is None")
+    else:
+        V = int(vocab_size)
+    wq_b, ws_b = packed_bytes(V, H, group_size)
+    if wq.numel() * wq.element_size() != wq_b or wscale.numel() * 4 != ws_b:
+        raise ValueError("wq / wscale sizes do not match a packed V x H head")
+    dev = act_q.device
+    values, indices = _outputs(dev, M, k, out)
+    ws = _workspace(dev, M, V, k, chunk_rows, workspace)
+    o = _opts(chunk_rows, score_event)
+    _check(_lib.lmtopk_binary(_ptr(act_q), _ptr(act_scale), _ptr(wq), _ptr(wscale), _ptr(bias),
+                              M, V, H, group_size, k, _ptr(values), _ptr(indices), _ptr(ws),
+                              ws.numel(), ctypes.byref(o), _stream(act_q)))
+    return values, indices
+
+
+def lm_head_topk_dense(hidden, weight, k=50, bias=None, *, chunk_rows=0, out=None,
+                       workspace=None, score_event=None):
+    """Exact top-k of hidden @ weight.T (+ bias); hidden and weight both fp32 or both bf16."""
+    _need_cuda("hidden", hidden, ndim=2)
+    _need_cuda("weight", weight, ndim=2)
+    if hidden.dtype != weight.dtype or hidden.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("hidden and weight must share dtype float32 or bfloat16")
+    M, H = hidden.shape
+    V, H2 = weight.shape
+    if H2 != H:
+        raise ValueError("hidden and weight disagree on H")
+    if bias is not None:
+        _need_cuda("bias", bias, torch.float32, 1)
+        if bias.numel() != V:
+            raise ValueError("bias must have V entries")
+    dev = hidden.device
+    values, indices = _outputs(dev, M, k, out)
+    ws = _workspace(dev, M, V, k, chunk_rows, workspace)
+    o = _opts(chunk_rows, score_event)
+    dt = _BF16 if hidden.dtype == torch.bfloat16 else _F32
+    _check(_lib.lmtopk_dense(_ptr(hidden), _ptr(weight), dt, _ptr(bias), M, V, H, k,
+                             _ptr(values), _ptr(indices), _ptr(ws), ws.numel(), ctypes.byref(o),
+                             _stream(hidden)))
+    return values, indices
+
+
+def topk_logits(logits, k, *, chunk_rows=0, out=None, workspace=None, score_event=None):
+    """The selection stage alone: exact top-k of each row of fp32 logits [M, V]."""
+    if not isinstance(logits, torch.Tensor) or logits.device.type != "cuda":
+        raise ValueError("logits must be a GPU tensor")
+    if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be float32 [M, V] with unit stride along V")
+    M, V = logits.shape
+    ld = logits.stride(0) if M > 1 else V
+    dev = logits.device
+    values, indices = _outputs(dev, M, k, out)
+    ws = _workspace(dev, M, V, k, chunk_rows, workspace)
+    o = _opts(chunk_rows, score_event)
+    _check(_lib.lmtopk_select(_ptr(logits), M, V, ld, k, _ptr(values), _ptr(indices), _ptr(ws),
+                              ws.numel(), ctypes.byref(o), _stream(logits)))
+    return values, indices

@@ -1,0 +1,61 @@
+// lmtopk_internal.hpp - interface between the C ABI (host validation and
+// geometry, plain C++) and the HIP translation unit (kernels and launchers).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lmtopk {
+
+constexpr int kMaxMergeLevels = 8;
+constexpr int64_t kSegMax = 16384;  // candidates one merge workgroup can hold (1024 x 16)
+
+struct MergeLevel {
+  int64_t n_in;  // candidates per row read by this level
+  int n_seg;     // segments per row (workgroups per row); 1 = final level
+  int rm;        // candidate slots per thread
+  int nw;        // waves per workgroup
+};
+
+// Chunking and merge plan of one call; identical for every path given
+// (M, V, k, chunk_rows).
+struct Geometry {
+  int64_t M, V;
+  int k;
+  int chunk_rows;  // C: vocabulary rows per chunk (workgroup)
+  int rpl;         // rows per lane: C = 64 * nw * rpl
+  int nw;          // waves per chunk workgroup
+  int n_chunks;
+  int kc;          // candidate slots per chunk per row = min(k, C)
+  int64_t n_tiles; // 64-row tiles covering V
+  int n_levels;
+  MergeLevel level[kMaxMergeLevels];
+  size_t region0_bytes;  // chunk candidates [M][n_chunks * kc] x 8 B
+  size_t region1_bytes;  // first intermediate merge output, or 0
+  size_t workspace_bytes;
+};
+
+// Returns 0 or an lmtopk_status code (SHAPE, K, OPTIONS).
+int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, Geometry* g);
+
+// Launchers; each returns a hipError_t value (0 = success).
+int launch_pack(const void* w, int w_is_bf16, int64_t V, int64_t H, void* wq, float* wscale,
+                void* stream);
+int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* act_scale,
+                         const void* wq, const float* wscale, const float* bias, int64_t H,
+                         void* workspace, void* stream);
+int launch_dense_chunks(const Geometry& g, const void* hidden, const void* weight, int is_bf16,
+                        const float* bias, int64_t H, void* workspace, void* stream);
+int launch_select_chunks(const Geometry& g, const float* logits, int64_t ld, void* workspace,
+                         void* stream);
+int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* indices,
+                  void* stream);
+int record_event(void* event, void* stream);
+// Largest LDS (bytes) one workgroup may use on the current device.
+int max_lds_per_block(size_t* bytes);
+
+// LDS bytes the scoring kernels need.
+size_t binary_lds_bytes(int64_t M, int64_t H);
+size_t dense_lds_bytes(int64_t M, int chunk_rows);
+
+}  // namespace lmtopk

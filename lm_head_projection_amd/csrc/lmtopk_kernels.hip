@@ -1,0 +1,715 @@
+// lmtopk_kernels.hip - HIP kernels for gfx950 (CDNA4, wave64) and their launchers.
+//
+// Kernels
+//   k_pack          pack a dense fp32/bf16 head into signs + group scales
+//                   (lm-head-topk page, sections "Usage" and "Requirements and
+//                   limits": binary weights are packed offline)
+//   k_binary_chunk  binary head: one workgroup scores one vocabulary chunk for
+//                   all M rows, streaming every packed weight byte once, and
+//                   selects that chunk's exact top-k (section "Method")
+//   k_dense_chunk   dense fp32/bf16 head, same structure (section "Usage",
+//                   dense entry point)
+//   k_select_chunk  the chunk selection fed from fp32 logits in memory
+//   k_merge         merges chunk candidates into the final sorted top-k
+//                   (section "Method", second pass), or into a smaller
+//                   candidate set when one workgroup cannot hold them all
+//
+// Candidates are (fp32 value bits, int32 index) pairs, index -1 = padding.
+// Every list of candidates is kept in ascending vocabulary index order, so
+// "lower index first" on ties reduces to "earlier position first".
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lmtopk_device.hpp"
+#include "lmtopk_internal.hpp"
+
+namespace lmtopk {
+
+constexpr int kGroup = 128;
+
+// ---------------------------------------------------------------------------
+// pack
+// ---------------------------------------------------------------------------
+// One wave per (64-row tile, quad of groups): lane r owns row 64 t + r and
+// reads its 4 x 128 weights itself (each lane a contiguous 512 B or 256 B),
+// so signs and the fp64 |w| sums need no cross-lane traffic.  Writes are one
+// uint4 of sign words per group and one float4 of scales per lane, coalesced
+// across the wave.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_pack(const void* __restrict__ w, int64_t V, int64_t H,
+                                              int64_t n_tiles, uint4* __restrict__ wq,
+                                              float4* __restrict__ wscale) {
+  const int lane = lane_id();
+  const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int G = (int)(H / kGroup);
+  const int Q = (G + 3) / 4;
+  if (wave_id >= n_tiles * Q) return;
+  const int64_t t = wave_id / Q;
+  const int q = (int)(wave_id - t * Q);
+  const int64_t v = t * 64 + lane;
+  const bool row_ok = v < V;
+  float sc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = 4 * q + i;
+    if (g >= G) break;
+    uint32_t word[4] = {0u, 0u, 0u, 0u};
+    double s = 0.0;
+    if (row_ok) {
+      if (BF16) {
+        const uint4* src = reinterpret_cast<const uint4*>(
+            static_cast<const uint16_t*>(w) + v * H + (int64_t)g * kGroup);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {  // 16 x 8 bf16
+          const uint4 x = src[c];
+          const uint32_t part[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t hbits = (part[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+            const float f = __uint_as_float(hbits << 16);
+            const int j = c * 8 + e;
+            word[j >> 5] |= (f >= 0.f ? 1u : 0u) << (j & 31);
+            s += (double)fabsf(f);
+          }
+        }
+      } else {
+        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(w) + v * H +
+                                                            (int64_t)g * kGroup);
+#pragma unroll
+        for (int c = 0; c < 32; ++c) {  // 32 x 4 fp32
+          const float4 x = src[c];
+          const float f4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = c * 4 + e;
+            word[j >> 5] |= (f4[e] >= 0.f ? 1u : 0u) << (j & 31);
+            s += (double)fabsf(f4[e]);
+          }
+        }
+      }
+      sc[i] = (float)(s / 128.0);
+    }
+    wq[((size_t)t * G + g) * 64 + lane] = make_uint4(word[0], word[1], word[2], word[3]);
+  }
+  wscale[((size_t)t * Q + q) * 64 + lane] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+}
+
+// ---------------------------------------------------------------------------
+// shared pieces of the chunk kernels
+// ---------------------------------------------------------------------------
+struct ChunkOut {
+  uint2* cand;   // [M][n_chunks][kc]
+  int n_chunks;
+  int kc;
+  int k;
+};
+
+// Selects the chunk's top-k of row m from RPL slots per lane and writes them
+// (ascending index) followed by padding up to kc entries.
+template <int RPL>
+__device__ __forceinline__ void chunk_select_write(const float (&val)[RPL], const int32_t (&idx)[RPL],
+                                                   uint32_t valid, int m, const ChunkOut& o,
+                                                   SelectSmem& sm) {
+  uint32_t key[RPL], vb[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    vb[r] = __float_as_uint(val[r]);
+    key[r] = float_key(val[r]);
+  }
+  const SelectRange s = block_select<RPL>(key, valid, (uint32_t)o.k, sm);
+  uint2* out = o.cand + ((size_t)m * o.n_chunks + blockIdx.x) * o.kc;
+  const uint32_t n = block_compact<RPL>(key, valid, s, vb, idx, sm,
+                                        [&](uint32_t pos, uint32_t bits, int32_t ix) {
+                                          out[pos] = make_uint2(bits, (uint32_t)ix);
+                                        });
+  for (int i = (int)n + (int)threadIdx.x; i < o.kc; i += blockDim.x)
+    out[i] = make_uint2(0u, 0xFFFFFFFFu);
+}
+
+// ---------------------------------------------------------------------------
+// binary chunk kernel
+// ---------------------------------------------------------------------------
+struct BinaryArgs {
+  const int8_t* act_q;     // [M][H]
+  const float* act_scale;  // [M]
+  const uint4* wq;         // packed signs, layout v1
+  const float4* wscale;    // packed scales, layout v1
+  const float* bias;       // [V] or null
+  int64_t V, H, n_tiles;
+  int G, Q;
+  int tiles_per_chunk;
+  ChunkOut out;
+};
+
+__device__ __forceinline__ uint32_t and_popc4(const uint4& w, const uint4& p) {
+  return __popc(w.x & p.x) + __popc(w.y & p.y) + __popc(w.z & p.z) + __popc(w.w & p.w);
+}
+
+__device__ __forceinline__ float comp4(const float4& f, int i) {
+  return i == 0 ? f.x : i == 1 ? f.y : i == 2 ? f.z : f.w;
+}
+
+// Lane r of wave w owns rows ((chunk * tiles_per_chunk + w * RPL + s) * 64 + r)
+// for s < RPL.  Per group g of 128 weights the lane loads one uint4 of sign
+// bits per row; per row m of activations, the group's exact integer dot is
+//   D = sum_j a_j * sign_j = 2 * S - A,  S = sum_j [bit_j] a_j,  A = sum_j a_j,
+// with S built from the 8 two's-complement bit planes of the activations:
+//   S = -128 * c_7 + sum_{p<7} 2^p * c_p,   c_p = popcount(bits AND plane_p),
+// and the fp32 logit accumulates fmaf((float)D, scale_g, acc) in ascending g.
+template <int M, int RPL>
+__global__ __launch_bounds__(1024) void k_binary_chunk(BinaryArgs a) {
+  extern __shared__ __align__(16) uint8_t dyn_lds[];
+  __shared__ SelectSmem ssm;
+  const int G = a.G;
+  uint4* planes = reinterpret_cast<uint4*>(dyn_lds);          // [M][G][8]
+  int* neg_a = reinterpret_cast<int*>(planes + (size_t)M * G * 8);  // [M][G]
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int nw = blockDim.x >> 6;
+
+  // activation bit planes: for 64 consecutive activations, bit p of every
+  // lane's value is one ballot = two plane words
+  for (int mg = wave; mg < M * G; mg += nw) {
+    const int m = mg / G;
+    const int g = mg - m * G;
+    const int8_t* src = a.act_q + (size_t)m * a.H + (size_t)g * kGroup;
+    const int a0 = src[lane];
+    const int a1 = src[64 + lane];
+    uint4 mine = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint64_t b0 = ballot((a0 >> p) & 1);
+      const uint64_t b1 = ballot((a1 >> p) & 1);
+      if (lane == p)
+        mine = make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1, (uint32_t)(b1 >> 32));
+    }
+    if (lane < 8) planes[((size_t)m * G + g) * 8 + lane] = mine;
+    int s = a0 + a1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    if (lane == 0) neg_a[m * G + g] = -s;
+  }
+  __syncthreads();
+
+  const int64_t tile0 = (int64_t)blockIdx.x * a.tiles_per_chunk + (int64_t)wave * RPL;
+  bool ok[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) ok[r] = (tile0 + r) < a.n_tiles;
+
+  float acc[RPL][M];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+
+  uint4 wc[4][RPL];
+  float4 sc[RPL];
+  auto load_quad = [&](int q, uint4 (&w)[4][RPL], float4 (&s)[RPL]) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      s[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i][r] = make_uint4(0u, 0u, 0u, 0u);
+      if (ok[r]) {
+        const int64_t t = tile0 + r;
+        s[r] = a.wscale[((size_t)t * a.Q + q) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int g = 4 * q + i;
+          if (g < G) w[i][r] = a.wq[((size_t)t * G + g) * 64 + lane];
+        }
+      }
+    }
+  };
+
+  load_quad(0, wc, sc);
+  for (int q = 0; q < a.Q; ++q) {
+    uint4 wn[4][RPL];
+    float4 sn[RPL];
+    if (q + 1 < a.Q) load_quad(q + 1, wn, sn);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = 4 * q + i;
+      if (g < G) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const uint4* P = planes + ((size_t)m * G + g) * 8;
+          uint4 pl[8];
+#pragma unroll
+          for (int p = 0; p < 8; ++p) pl[p] = P[p];
+          const int na = neg_a[m * G + g];
+#pragma unroll
+          for (int r = 0; r < RPL; ++r) {
+            const uint4 w = wc[i][r];
+            int S = -(int)and_popc4(w, pl[7]);
+#pragma unroll
+            for (int p = 6; p >= 0; --p) S = 2 * S + (int)and_popc4(w, pl[p]);
+            const int D = 2 * S + na;
+            acc[r][m] = fmaf((float)D, comp4(sc[r], i), acc[r][m]);
+          }
+        }
+      }
+    }
+    if (q + 1 < a.Q) {
+#pragma unroll
+      for (int r = 0; r < RPL; ++r) {
+        sc[r] = sn[r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wc[i][r] = wn[i][r];
+      }
+    }
+  }
+
+  int32_t idx[RPL];
+  uint32_t valid = 0u;
+  float bias_v[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int64_t v = (tile0 + r) * 64 + lane;
+    idx[r] = (int32_t)v;
+    const bool vv = ok[r] && v < a.V;
+    valid |= (vv ? 1u : 0u) << r;
+    bias_v[r] = (a.bias != nullptr && vv) ? a.bias[v] : 0.f;
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const float s = a.act_scale[m];
+    float val[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) val[r] = fmaf(acc[r][m], s, bias_v[r]);
+    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dense chunk kernel
+// ---------------------------------------------------------------------------
+struct DenseArgs {
+  const uint8_t* hidden;  // [M][H] fp32 or bf16
+  const uint8_t* weight;  // [V][H] fp32 or bf16
+  const float* bias;
+  int64_t V, H;
+  int chunk_rows;
+  ChunkOut out;
+};
+
+template <bool BF16>
+__device__ __forceinline__ float dot16(const uint4& h, const uint4& w, float acc) {
+  if (BF16) {
+    const uint32_t hp[4] = {h.x, h.y, h.z, h.w};
+    const uint32_t wp[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__uint_as_float(hp[e] << 16), __uint_as_float(wp[e] << 16), acc);
+      acc = fmaf(__uint_as_float(hp[e] & 0xFFFF0000u), __uint_as_float(wp[e] & 0xFFFF0000u), acc);
+    }
+  } else {
+    acc = fmaf(__uint_as_float(h.x), __uint_as_float(w.x), acc);
+    acc = fmaf(__uint_as_float(h.y), __uint_as_float(w.y), acc);
+    acc = fmaf(__uint_as_float(h.z), __uint_as_float(w.z), acc);
+    acc = fmaf(__uint_as_float(h.w), __uint_as_float(w.w), acc);
+  }
+  return acc;
+}
+
+// One wave computes one vocabulary row at a time (two rows interleaved):
+// lane l takes the 16-byte vectors l, l+64, ... of the row, accumulates in
+// fp32 in that order, then an xor-butterfly over the 64 lanes gives the row
+// sum (the same tree for every row).  Scores go to LDS; the chunk selection
+// reads them back one row per lane slot.
+template <int M, bool BF16, int RPL>
+__global__ __launch_bounds__(1024) void k_dense_chunk(DenseArgs a) {
+  extern __shared__ __align__(16) uint8_t dyn_lds[];
+  __shared__ SelectSmem ssm;
+  float* scores = reinterpret_cast<float*>(dyn_lds);  // [M][C]
+  const int C = a.chunk_rows;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int esz = BF16 ? 2 : 4;
+  const int64_t nvec = a.H * esz / 16;
+  const int64_t row_bytes = a.H * esz;
+  const int64_t base = (int64_t)blockIdx.x * C;
+  const int rows_per_wave = 64 * RPL;
+
+  for (int rr = 0; rr < rows_per_wave; rr += 2) {
+    const int lr0 = wave * rows_per_wave + rr;
+    const int64_t v0 = base + lr0, v1 = v0 + 1;
+    const bool ok0 = v0 < a.V, ok1 = v1 < a.V;
+    if (!ok0) break;  // rows are in increasing order
+    float acc0[M], acc1[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc0[m] = acc1[m] = 0.f;
+    const uint4* w0 = reinterpret_cast<const uint4*>(a.weight + v0 * row_bytes);
+    const uint4* w1 = reinterpret_cast<const uint4*>(a.weight + (ok1 ? v1 : v0) * row_bytes);
+#pragma unroll 2
+    for (int64_t i = lane; i < nvec; i += 64) {
+      const uint4 x0 = w0[i];
+      const uint4 x1 = w1[i];
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const uint4 h = reinterpret_cast<const uint4*>(a.hidden + (int64_t)m * row_bytes)[i];
+        acc0[m] = dot16<BF16>(h, x0, acc0[m]);
+        acc1[m] = dot16<BF16>(h, x1, acc1[m]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float s0 = acc0[m], s1 = acc1[m];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        s0 += __shfl_xor(s0, o);
+        s1 += __shfl_xor(s1, o);
+      }
+      if (lane == 0) {
+        scores[m * C + lr0] = s0 + (a.bias ? a.bias[v0] : 0.f);
+        if (ok1) scores[m * C + lr0 + 1] = s1 + (a.bias ? a.bias[v1] : 0.f);
+      }
+    }
+  }
+  __syncthreads();
+
+  int32_t idx[RPL];
+  uint32_t valid = 0u;
+  int lr[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    lr[r] = (wave * RPL + r) * 64 + lane;
+    const int64_t v = base + lr[r];
+    idx[r] = (int32_t)v;
+    valid |= (v < a.V ? 1u : 0u) << r;
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float val[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) val[r] = ((valid >> r) & 1u) ? scores[m * C + lr[r]] : 0.f;
+    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// selection-only chunk kernel (scores read from fp32 logits)
+// ---------------------------------------------------------------------------
+struct SelectArgs {
+  const float* logits;  // [M][ld]
+  int64_t M, V, ld;
+  int chunk_rows;
+  ChunkOut out;
+};
+
+template <int RPL>
+__global__ __launch_bounds__(1024) void k_select_chunk(SelectArgs a) {
+  __shared__ SelectSmem ssm;
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int64_t base = (int64_t)blockIdx.x * a.chunk_rows;
+  int32_t idx[RPL];
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int64_t v = base + (wave * RPL + r) * 64 + lane;
+    idx[r] = (int32_t)v;
+    valid |= (v < a.V ? 1u : 0u) << r;
+  }
+  for (int m = 0; m < (int)a.M; ++m) {
+    const float* row = a.logits + (size_t)m * a.ld;
+    float val[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) val[r] = ((valid >> r) & 1u) ? row[idx[r]] : 0.f;
+    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge
+// ---------------------------------------------------------------------------
+struct MergeArgs {
+  const uint2* in;  // [M][n_in] candidates, ascending index within each row
+  int64_t n_in;
+  int k;
+  int n_seg;        // segments per row; blockIdx.x = segment, blockIdx.y = row
+  int64_t seg;      // candidates per segment
+  uint2* out;       // intermediate: [M][n_seg][k]
+  float* values;    // final: [M][k]
+  int64_t* indices; // final: [M][k]
+};
+
+// Workgroup (segment s, row m) takes candidates [s*seg, (s+1)*seg) of row m,
+// RM slots per thread (slot order = candidate order = index order), selects
+// their exact top-k and either writes them in index order (intermediate
+// level) or sorts them by (value desc, index asc) through rank counting --
+// each entry's output position is the number of entries ahead of it -- and
+// writes values / indices (final level).
+template <int RM>
+__global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
+  __shared__ SelectSmem ssm;
+  __shared__ uint32_t f_key[kMaxK];
+  __shared__ uint32_t f_bits[kMaxK];
+  __shared__ int32_t f_idx[kMaxK];
+  const int wave = threadIdx.x >> 6;
+  const int lane = lane_id();
+  const int m = blockIdx.y;
+  const int64_t s0 = (int64_t)blockIdx.x * a.seg;
+  const uint2* in = a.in + (size_t)m * a.n_in;
+  uint32_t key[RM], vb[RM];
+  int32_t idx[RM];
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    const int64_t local = (int64_t)(wave * RM + r) * 64 + lane;
+    const int64_t pos = s0 + local;
+    uint2 e = make_uint2(0u, 0xFFFFFFFFu);
+    if (local < a.seg && pos < a.n_in) e = in[pos];
+    vb[r] = e.x;
+    idx[r] = (int32_t)e.y;
+    key[r] = float_key(__uint_as_float(e.x));
+    valid |= (idx[r] >= 0 ? 1u : 0u) << r;
+  }
+  const SelectRange s = block_select<RM>(key, valid, (uint32_t)a.k, ssm);
+  if (a.n_seg > 1) {
+    uint2* out = a.out + ((size_t)m * a.n_seg + blockIdx.x) * a.k;
+    const uint32_t n = block_compact<RM>(key, valid, s, vb, idx, ssm,
+                                         [&](uint32_t pos, uint32_t bits, int32_t ix) {
+                                           out[pos] = make_uint2(bits, (uint32_t)ix);
+                                         });
+    for (int i = (int)n + (int)threadIdx.x; i < a.k; i += blockDim.x)
+      out[i] = make_uint2(0u, 0xFFFFFFFFu);
+    return;
+  }
+  const uint32_t n = block_compact<RM>(key, valid, s, vb, idx, ssm,
+                                       [&](uint32_t pos, uint32_t bits, int32_t ix) {
+                                         f_key[pos] = float_key(__uint_as_float(bits));
+                                         f_bits[pos] = bits;
+                                         f_idx[pos] = ix;
+                                       });
+  __syncthreads();
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint32_t ki = f_key[i];
+    const int32_t ii = f_idx[i];
+    uint32_t rank = 0;
+    for (uint32_t j = 0; j < n; ++j) {
+      const uint32_t kj = f_key[j];
+      rank += (kj > ki || (kj == ki && f_idx[j] < ii)) ? 1u : 0u;
+    }
+    if (rank < (uint32_t)a.k) {
+      a.values[(size_t)m * a.k + rank] = __uint_as_float(f_bits[i]);
+      a.indices[(size_t)m * a.k + rank] = (int64_t)ii;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+namespace {
+
+template <typename Arg>
+hipError_t launch1(void (*kern)(Arg), dim3 grid, dim3 block, size_t lds, void* stream, Arg arg) {
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  void* args[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, args, lds,
+                         static_cast<hipStream_t>(stream));
+}
+
+template <int M>
+void (*binary_kernel_m(int rpl))(BinaryArgs) {
+  switch (rpl) {
+    case 1: return k_binary_chunk<M, 1>;
+    case 2: return k_binary_chunk<M, 2>;
+    case 4: return k_binary_chunk<M, 4>;
+  }
+  return nullptr;
+}
+
+void (*binary_kernel(int M, int rpl))(BinaryArgs) {
+  switch (M) {
+    case 1: return binary_kernel_m<1>(rpl);
+    case 2: return binary_kernel_m<2>(rpl);
+    case 3: return binary_kernel_m<3>(rpl);
+    case 4: return binary_kernel_m<4>(rpl);
+    case 5: return binary_kernel_m<5>(rpl);
+    case 6: return binary_kernel_m<6>(rpl);
+    case 7: return binary_kernel_m<7>(rpl);
+    case 8: return binary_kernel_m<8>(rpl);
+  }
+  return nullptr;
+}
+
+template <int M, bool BF16>
+void (*dense_kernel_mb(int rpl))(DenseArgs) {
+  switch (rpl) {
+    case 1: return k_dense_chunk<M, BF16, 1>;
+    case 2: return k_dense_chunk<M, BF16, 2>;
+    case 4: return k_dense_chunk<M, BF16, 4>;
+  }
+  return nullptr;
+}
+
+template <bool BF16>
+void (*dense_kernel_b(int M, int rpl))(DenseArgs) {
+  switch (M) {
+    case 1: return dense_kernel_mb<1, BF16>(rpl);
+    case 2: return dense_kernel_mb<2, BF16>(rpl);
+    case 3: return dense_kernel_mb<3, BF16>(rpl);
+    case 4: return dense_kernel_mb<4, BF16>(rpl);
+    case 5: return dense_kernel_mb<5, BF16>(rpl);
+    case 6: return dense_kernel_mb<6, BF16>(rpl);
+    case 7: return dense_kernel_mb<7, BF16>(rpl);
+    case 8: return dense_kernel_mb<8, BF16>(rpl);
+  }
+  return nullptr;
+}
+
+void (*select_kernel(int rpl))(SelectArgs) {
+  switch (rpl) {
+    case 1: return k_select_chunk<1>;
+    case 2: return k_select_chunk<2>;
+    case 4: return k_select_chunk<4>;
+  }
+  return nullptr;
+}
+
+void (*merge_kernel(int rm))(MergeArgs) {
+  switch (rm) {
+    case 1: return k_merge<1>;
+    case 2: return k_merge<2>;
+    case 4: return k_merge<4>;
+    case 8: return k_merge<8>;
+    case 12: return k_merge<12>;
+    case 16: return k_merge<16>;
+  }
+  return nullptr;
+}
+
+ChunkOut chunk_out(const Geometry& g, void* workspace) {
+  ChunkOut o;
+  o.cand = static_cast<uint2*>(workspace);
+  o.n_chunks = g.n_chunks;
+  o.kc = g.kc;
+  o.k = g.k;
+  return o;
+}
+
+}  // namespace
+
+size_t binary_lds_bytes(int64_t M, int64_t H) {
+  const int64_t G = H / kGroup;
+  return (size_t)(M * G * 8 * 16 + M * G * 4);
+}
+
+size_t dense_lds_bytes(int64_t M, int chunk_rows) { return (size_t)(M * chunk_rows * 4); }
+
+int max_lds_per_block(size_t* bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  int v = 0;
+  e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return (int)e;
+  *bytes = (size_t)v;
+  return 0;
+}
+
+int launch_pack(const void* w, int w_is_bf16, int64_t V, int64_t H, void* wq, float* wscale,
+                void* stream) {
+  const int64_t n_tiles = (V + 63) / 64;
+  const int64_t G = H / kGroup;
+  const int64_t waves = n_tiles * ((G + 3) / 4);
+  const dim3 grid((unsigned)((waves + 3) / 4));
+  const dim3 block(256);
+  const void* a_w = w;
+  int64_t a_V = V, a_H = H, a_tiles = n_tiles;
+  uint4* a_wq = static_cast<uint4*>(wq);
+  float4* a_ws = reinterpret_cast<float4*>(wscale);
+  void* args[] = {&a_w, &a_V, &a_H, &a_tiles, &a_wq, &a_ws};
+  const void* kern = w_is_bf16 ? reinterpret_cast<const void*>(k_pack<true>)
+                               : reinterpret_cast<const void*>(k_pack<false>);
+  return (int)hipLaunchKernel(kern, grid, block, args, 0, static_cast<hipStream_t>(stream));
+}
+
+int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* act_scale,
+                         const void* wq, const float* wscale, const float* bias, int64_t H,
+                         void* workspace, void* stream) {
+  BinaryArgs a;
+  a.act_q = act_q;
+  a.act_scale = act_scale;
+  a.wq = static_cast<const uint4*>(wq);
+  a.wscale = reinterpret_cast<const float4*>(wscale);
+  a.bias = bias;
+  a.V = g.V;
+  a.H = H;
+  a.n_tiles = g.n_tiles;
+  a.G = (int)(H / kGroup);
+  a.Q = (a.G + 3) / 4;
+  a.tiles_per_chunk = g.chunk_rows / 64;
+  a.out = chunk_out(g, workspace);
+  auto kern = binary_kernel((int)g.M, g.rpl);
+  if (!kern) return (int)hipErrorInvalidValue;
+  return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), binary_lds_bytes(g.M, H), stream, a);
+}
+
+int launch_dense_chunks(const Geometry& g, const void* hidden, const void* weight, int is_bf16,
+                        const float* bias, int64_t H, void* workspace, void* stream) {
+  DenseArgs a;
+  a.hidden = static_cast<const uint8_t*>(hidden);
+  a.weight = static_cast<const uint8_t*>(weight);
+  a.bias = bias;
+  a.V = g.V;
+  a.H = H;
+  a.chunk_rows = g.chunk_rows;
+  a.out = chunk_out(g, workspace);
+  auto kern = is_bf16 ? dense_kernel_b<true>((int)g.M, g.rpl) : dense_kernel_b<false>((int)g.M, g.rpl);
+  if (!kern) return (int)hipErrorInvalidValue;
+  return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), dense_lds_bytes(g.M, g.chunk_rows),
+                      stream, a);
+}
+
+int launch_select_chunks(const Geometry& g, const float* logits, int64_t ld, void* workspace,
+                         void* stream) {
+  SelectArgs a;
+  a.logits = logits;
+  a.M = g.M;
+  a.V = g.V;
+  a.ld = ld;
+  a.chunk_rows = g.chunk_rows;
+  a.out = chunk_out(g, workspace);
+  auto kern = select_kernel(g.rpl);
+  if (!kern) return (int)hipErrorInvalidValue;
+  return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), 0, stream, a);
+}
+
+int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* indices,
+                  void* stream) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint2* regions[2] = {reinterpret_cast<uint2*>(ws), reinterpret_cast<uint2*>(ws + g.region0_bytes)};
+  for (int l = 0; l < g.n_levels; ++l) {
+    const MergeLevel& L = g.level[l];
+    MergeArgs a;
+    a.in = regions[l & 1];
+    a.n_in = L.n_in;
+    a.k = g.k;
+    a.n_seg = L.n_seg;
+    a.seg = (int64_t)L.nw * 64 * L.rm;
+    a.out = regions[(l + 1) & 1];
+    a.values = values;
+    a.indices = indices;
+    auto kern = merge_kernel(L.rm);
+    if (!kern) return (int)hipErrorInvalidValue;
+    const hipError_t e = launch1(kern, dim3(L.n_seg, (unsigned)g.M), dim3(64 * L.nw), 0, stream, a);
+    if (e != hipSuccess) return (int)e;
+  }
+  return 0;
+}
+
+int record_event(void* event, void* stream) {
+  return (int)hipEventRecord(static_cast<hipEvent_t>(event), static_cast<hipStream_t>(stream));
+}
+
+}  // namespace lmtopk

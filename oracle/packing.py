@@ -39,9 +39,10 @@ def pack_logical(W):
     W = np.asarray(W, dtype=np.float32)
     V, H = W.shape
     assert H % GROUP == 0
-    signs = np.where(W >= 0, 1, -1).astype(np.int8)
-    absw = np.abs(W.astype(np.float64)).reshape(V, H // GROUP, GROUP)
-    scales = (absw.sum(axis=2) / GROUP).astype(np.float32)
+    signs = np.where(W >= 0, np.int8(1), np.int8(-1))
+    # |w| is exact in fp32; each group is summed in float64
+    sums = np.abs(W).reshape(V, H // GROUP, GROUP).sum(axis=2, dtype=np.float64)
+    scales = (sums / GROUP).astype(np.float32)
     return signs, scales
 
 

@@ -69,13 +69,19 @@ def project_binary(act_q, act_scale, signs, scales, bias=None, block_rows=4096):
     a = np.asarray(act_q).astype(np.float64)
     x = a * np.asarray(act_scale, dtype=np.float64)[:, None]
     s = np.asarray(signs)
-    sc = np.asarray(scales)
+    sc = np.asarray(scales, dtype=np.float32)
     V, H = s.shape
-    assert x.shape[1] == H
+    assert x.shape[1] == H and H % GROUP == 0
     out = np.empty((x.shape[0], V), dtype=np.float64)
+    buf = np.empty((min(block_rows, V), H), dtype=np.float64)
     for v0 in range(0, V, block_rows):
-        wd = dequantize_binary(s[v0:v0 + block_rows], sc[v0:v0 + block_rows])
-        out[:, v0:v0 + wd.shape[0]] = x @ wd.T
+        n = min(block_rows, V - v0)
+        wd = buf[:n]
+        # dequantized block, written in place: sign[v, j] * scale[v, j // 128]
+        np.multiply(s[v0:v0 + n].reshape(n, H // GROUP, GROUP),
+                    sc[v0:v0 + n, :, None].astype(np.float64),
+                    out=wd.reshape(n, H // GROUP, GROUP))
+        out[:, v0:v0 + n] = x @ wd.T
     if bias is not None:
         out += np.asarray(bias, dtype=np.float64)[None, :]
     return out

@@ -1,0 +1,112 @@
+"""Comparison rules between the HIP path and the CPU oracle (test helpers).
+
+Selection on given fp32 logits must be bit-exact.  End-to-end (projection +
+selection) results are compared with the rules below, which follow from the
+fp32 arithmetic of the GPU path and the pages' tolerances (lm-head-topk page,
+section "Correctness": values to 1e-5 dense and 1e-2 binary against a
+dequantized reference; indices equal to the reference):
+
+  * every GPU value is within rtol of the oracle's fp64 logit of that same
+    index, and within the a-priori fp32 error bound eps of it;
+  * the GPU output is in its own (value desc, index asc) order;
+  * where the oracle's gap between the k-th and (k+1)-th value exceeds 1e-4
+    relative, the GPU index set equals the oracle's; in any case no GPU index
+    may be more than 2 eps below the oracle's k-th value;
+  * position by position, the GPU index equals the oracle's unless the two
+    oracle values there are within 2 eps of each other (a pair the fp32
+    rounding may legitimately order either way).
+eps for entry (m, v) is the bound of a sequence of n fp32 roundings over
+terms of total magnitude mag: n * 2^-24 * mag, with n and mag given by the
+caller for its accumulation order.
+"""
+
+import numpy as np
+
+import oracle
+
+U = 2.0 ** -24
+
+
+def assert_select_exact(logits, vals, idx, k):
+    """GPU selection on fp32 logits [M, V] equals the oracle bit for bit."""
+    logits = np.asarray(logits, dtype=np.float32)
+    for m in range(logits.shape[0]):
+        ov, oi = oracle.topk_stable(logits[m], k)
+        assert np.array_equal(idx[m], oi), f"row {m}: indices differ\n gpu {idx[m][:20]}\n ora {oi[:20]}"
+        assert np.array_equal(np.asarray(vals[m], np.float32).view(np.uint32), ov.view(np.uint32)), \
+            f"row {m}: value bits differ"
+        ok, why = oracle.certify_topk(logits[m], vals[m].astype(np.float32), idx[m], k)
+        assert ok, f"row {m}: certificate failed: {why}"
+
+
+def compare_end_to_end(L, vals, idx, k, rtol, eps_fn, floor_rel=1e-3):
+    """Check GPU (vals, idx) [M, k] against oracle fp64 logits L [M, V].
+
+    eps_fn(m, indices) -> array of fp32 error bounds for those entries.
+    Returns the number of positions where the GPU order differs from the
+    oracle's within the rounding allowance (informational).
+    """
+    L = np.asarray(L, dtype=np.float64)
+    M, V = L.shape
+    relaxed = 0
+    for m in range(M):
+        gi = np.asarray(idx[m], dtype=np.int64)
+        gv = np.asarray(vals[m], dtype=np.float64)
+        assert gi.shape == (k,)
+        assert np.all((gi >= 0) & (gi < V)), f"row {m}: index out of range"
+        assert np.unique(gi).shape[0] == k, f"row {m}: duplicate index"
+        kk = min(k + 1, V)
+        ov, oi = oracle.topk_stable(L[m], kk)
+        ref = L[m, gi]
+        eps = np.asarray(eps_fn(m, gi), dtype=np.float64)
+        floor = floor_rel * abs(ov[0])
+        err = np.abs(gv - ref)
+        assert np.all(err <= rtol * np.maximum(np.abs(ref), floor)), \
+            f"row {m}: value error {err.max():.3e} beyond rtol {rtol}"
+        assert np.all(err <= eps + 1e-300), f"row {m}: value error beyond the fp32 bound"
+        for i in range(k - 1):
+            a, b = gv[i], gv[i + 1]
+            assert a > b or (a == b and gi[i] < gi[i + 1]), f"row {m}: GPU output not ordered at {i}"
+        vk = ov[k - 1]
+        eps_o = np.asarray(eps_fn(m, oi[:k]), dtype=np.float64)
+        if kk > k:
+            gap = (ov[k - 1] - ov[k]) / max(abs(ov[k - 1]), 1e-300)
+            if gap > 1e-4:
+                assert set(gi.tolist()) == set(oi[:k].tolist()), f"row {m}: index set differs (gap {gap:.2e})"
+        assert np.all(ref >= vk - 2 * np.maximum(eps, eps_o[-1])), f"row {m}: an index far below the k-th"
+        for i in range(k):
+            if gi[i] != oi[i]:
+                tol = 2 * max(eps[i], eps_o[i])
+                assert abs(ref[i] - ov[i]) <= tol, \
+                    f"row {m} pos {i}: gpu idx {gi[i]} (L={ref[i]!r}) vs oracle {oi[i]} (L={ov[i]!r})"
+                relaxed += 1
+    return relaxed
+
+
+def binary_eps_fn(act_q, act_scale, signs_scales_fn, bias, G):
+    """fp32 bound for the binary logits: (G + 2) roundings over
+    act_scale * sum_j |a_j| * scale_g(j) + |bias|."""
+    aq = np.abs(np.asarray(act_q, dtype=np.float64))
+    asc = np.asarray(act_scale, dtype=np.float64)
+
+    def fn(m, ix):
+        sc = signs_scales_fn(ix)  # [n, G] fp32 scales of those rows
+        per_group = aq[m].reshape(G, 128).sum(axis=1)
+        mag = asc[m] * (np.asarray(sc, dtype=np.float64) @ per_group)
+        if bias is not None:
+            mag = mag + np.abs(np.asarray(bias, dtype=np.float64)[ix])
+        return (G + 2) * U * mag
+    return fn
+
+
+def dense_eps_fn(hidden_f32, weight_rows_fn, bias, H):
+    """fp32 bound for the dense logits: (H/64 + 8) roundings over sum_j |h_j w_j| + |bias|."""
+    h = np.abs(np.asarray(hidden_f32, dtype=np.float64))
+
+    def fn(m, ix):
+        w = np.abs(np.asarray(weight_rows_fn(ix), dtype=np.float64))
+        mag = w @ h[m]
+        if bias is not None:
+            mag = mag + np.abs(np.asarray(bias, dtype=np.float64)[ix])
+        return (H / 64 + 8) * U * mag
+    return fn

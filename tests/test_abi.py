@@ -1,0 +1,145 @@
+"""The C ABI on the host (CPU only): the library loads, exports every function
+include/lmtopk.h declares, and rejects every invalid argument with its status
+code before any HIP call.  Pointer arguments here are small fabricated
+integers that the library must never dereference."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import lm_head_projection_amd as lt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmtopk.h")
+
+OK, NULL, SHAPE, K, GROUP, DTYPE, ALIGN, WORKSPACE, OPTIONS, HIP = range(10)
+A = 4096      # a fabricated, 16-byte aligned "device pointer"
+ODD = 4100    # a fabricated, misaligned one
+BIG = 1 << 40
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lmtopk_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert {"lmtopk_pack_binary", "lmtopk_binary", "lmtopk_dense", "lmtopk_select"} <= set(names)
+    lib = ctypes.CDLL(lt.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", lt.library_path()], capture_output=True,
+                         text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), f"{n} not exported"
+
+
+def test_layout_and_sizes():
+    assert lt.layout_version() == 1
+    assert lt.packed_bytes(248320, 5120) == (158924800, 39731200)   # signs + fp32 scales
+    assert lt.packed_bytes(32001, 2048) == (32064 * 2048 // 8, 32064 * 16 * 4)
+    assert lt.packed_bytes(1, 640) == (64 * 640 // 8, 64 * 8 * 4)   # G=5 pads to 8 scales
+    # chunk candidates of the flagship: 243 chunks x 50 x 8 B, rounded to 256
+    assert lt.workspace_bytes(1, 248320, 50) == 97280
+    # k >= chunk rows: every chunk offers all its rows, and the merge needs two levels
+    assert lt.workspace_bytes(8, 248320, 1024) == 8 * 243 * 1024 * 8 + 8 * 16 * 1024 * 8
+
+
+def test_status_strings():
+    lib = lt._lib
+    for s in range(10):
+        assert lib.lmtopk_status_string(s)
+    assert lib.lmtopk_status_string(99) == b"unknown status"
+
+
+def _binary(**kw):
+    a = dict(act_q=A, act_scale=A, wq=A, wscale=A, bias=None, M=1, V=1000, H=256, group=128,
+             k=10, values=A, indices=A, ws=A, ws_bytes=BIG, opt=None, stream=None)
+    a.update(kw)
+    return lt._lib.lmtopk_binary(a["act_q"], a["act_scale"], a["wq"], a["wscale"], a["bias"],
+                                 a["M"], a["V"], a["H"], a["group"], a["k"], a["values"],
+                                 a["indices"], a["ws"], a["ws_bytes"], a["opt"], a["stream"])
+
+
+def _dense(**kw):
+    a = dict(hidden=A, weight=A, dtype=0, bias=None, M=2, V=1000, H=256, k=10, values=A,
+             indices=A, ws=A, ws_bytes=BIG, opt=None, stream=None)
+    a.update(kw)
+    return lt._lib.lmtopk_dense(a["hidden"], a["weight"], a["dtype"], a["bias"], a["M"], a["V"],
+                                a["H"], a["k"], a["values"], a["indices"], a["ws"],
+                                a["ws_bytes"], a["opt"], a["stream"])
+
+
+def _select(**kw):
+    a = dict(logits=A, M=1, V=1000, ld=1000, k=10, values=A, indices=A, ws=A, ws_bytes=BIG,
+             opt=None, stream=None)
+    a.update(kw)
+    return lt._lib.lmtopk_select(a["logits"], a["M"], a["V"], a["ld"], a["k"], a["values"],
+                                 a["indices"], a["ws"], a["ws_bytes"], a["opt"], a["stream"])
+
+
+def opt(chunk_rows=0, reserved=0):
+    return ctypes.byref(lt._Options(chunk_rows, reserved, None))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(act_q=None), NULL), (dict(wscale=None), NULL), (dict(values=None), NULL),
+    (dict(M=0), SHAPE), (dict(M=9), SHAPE), (dict(V=0), SHAPE), (dict(V=1 << 31), SHAPE),
+    (dict(H=0), SHAPE), (dict(M=8, H=8320), SHAPE),
+    (dict(k=0), K), (dict(k=2049, V=5000), K), (dict(k=11, V=10), K),
+    (dict(group=64), GROUP), (dict(H=200), GROUP),
+    (dict(act_q=ODD), ALIGN), (dict(wq=ODD), ALIGN), (dict(bias=ODD), ALIGN), (dict(values=ODD), ALIGN),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
+    (dict(opt=opt(100)), OPTIONS), (dict(opt=opt(8192)), OPTIONS), (dict(opt=opt(0, 1)), OPTIONS),
+])
+def test_binary_rejects(kw, code):
+    assert _binary(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=None), NULL), (dict(weight=None), NULL), (dict(indices=None), NULL),
+    (dict(M=9), SHAPE), (dict(H=0), SHAPE), (dict(k=0), K), (dict(dtype=2), DTYPE),
+    (dict(H=6), ALIGN), (dict(H=4, dtype=1), ALIGN), (dict(weight=ODD), ALIGN),
+    (dict(ws_bytes=0), WORKSPACE), (dict(opt=opt(-64)), OPTIONS),
+])
+def test_dense_rejects(kw, code):
+    assert _dense(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), NULL), (dict(ld=999), SHAPE), (dict(M=0), SHAPE), (dict(k=1001), K),
+    (dict(logits=ODD), ALIGN), (dict(ws=None), WORKSPACE), (dict(opt=opt(3000)), OPTIONS),
+])
+def test_select_rejects(kw, code):
+    assert _select(**kw) == code
+
+
+def test_pack_and_size_query_rejects():
+    lib = lt._lib
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.lmtopk_packed_bytes(10, 128, 128, None, ctypes.byref(b)) == NULL
+    assert lib.lmtopk_packed_bytes(0, 128, 128, ctypes.byref(a), ctypes.byref(b)) == SHAPE
+    assert lib.lmtopk_packed_bytes(10, 130, 128, ctypes.byref(a), ctypes.byref(b)) == GROUP
+    assert lib.lmtopk_pack_binary(None, 0, 10, 128, 128, A, A, None) == NULL
+    assert lib.lmtopk_pack_binary(A, 5, 10, 128, 128, A, A, None) == DTYPE
+    assert lib.lmtopk_pack_binary(A, 0, 10, 100, 128, A, A, None) == GROUP
+    assert lib.lmtopk_pack_binary(A, 0, 10, 128, 128, ODD, A, None) == ALIGN
+    n = ctypes.c_size_t()
+    assert lib.lmtopk_workspace_bytes(1, 100, 0, None, ctypes.byref(n)) == K
+    assert lib.lmtopk_workspace_bytes(1, 100, 5, opt(65), ctypes.byref(n)) == OPTIONS
+    assert lib.lmtopk_workspace_bytes(1, 100, 5, None, None) == NULL
+
+
+def test_python_binding_checks_before_the_library():
+    import torch
+    with pytest.raises((ValueError, TypeError)):
+        lt.lm_head_topk_binary(torch.zeros(1, 128, dtype=torch.int8), torch.ones(1),
+                               torch.zeros(16, dtype=torch.uint8), torch.zeros(4), k=1,
+                               vocab_size=1)
+    with pytest.raises(ValueError):
+        lt.topk_logits(torch.zeros(2, 10), 3)

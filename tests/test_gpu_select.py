@@ -1,0 +1,126 @@
+"""Selection stage on fp32 logits: bit-exact against the oracle (GPU).
+
+The chunk select and merge kernels are the ones the fused paths use; here
+they are fed from logits in memory so every result can be compared bit for
+bit (lm-head-topk page, section "Method": per-chunk top-k and a merge; ties to
+the lower index; section "Correctness": k = 1 is the argmax, ragged last
+chunk, all winners in one chunk, repeated calls identical).
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic
+from parity import assert_select_exact
+
+pytestmark = pytest.mark.gpu
+
+import lm_head_projection_amd as lt  # noqa: E402
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def run_select(logits_np, k, chunk_rows=0):
+    v, i = lt.topk_logits(dev(logits_np), k, chunk_rows=chunk_rows)
+    torch.cuda.synchronize()
+    return v.cpu().numpy(), i.cpu().numpy()
+
+
+def test_tiny_brute_force_patterns():
+    alphabet = np.array([-1.0, -0.0, 0.0, 1.0, 2.0], dtype=np.float32)
+    for V in range(1, 5):
+        pats = np.array(list(itertools.product(range(5), repeat=V)))
+        # batch the patterns as rows of M <= 8
+        for s in range(0, len(pats), 8):
+            rows = alphabet[pats[s:s + 8]]
+            for k in range(1, V + 1):
+                v, i = run_select(rows, k)
+                assert_select_exact(rows, v, i, k)
+
+
+@pytest.mark.parametrize("k", [1, 7, 50, 64, 1024, 2048])
+@pytest.mark.parametrize("chunk_rows", [0, 64, 256, 1024, 2048, 4096])
+def test_random_rows_all_chunk_sizes(k, chunk_rows):
+    x = synthetic.random_logits(3, 50000, seed=11)
+    v, i = run_select(x, k, chunk_rows)
+    assert_select_exact(x, v, i, k)
+
+
+@pytest.mark.parametrize("ties", [3, 20, 200])
+@pytest.mark.parametrize("k", [1, 50, 999])
+def test_heavy_ties_and_signed_zeros(ties, k):
+    x = synthetic.random_logits(4, 32001, seed=ties, ties=ties, signed_zeros=True)
+    v, i = run_select(x, k)
+    assert_select_exact(x, v, i, k)
+    v2, i2 = run_select(x, k, chunk_rows=512)
+    assert np.array_equal(i, i2) and np.array_equal(v.view(np.uint32), v2.view(np.uint32))
+
+
+def test_infinities_and_all_equal():
+    x = synthetic.random_logits(4, 5000, seed=3)
+    x[0, ::97] = np.inf
+    x[1, ::13] = -np.inf
+    x[2, :] = np.float32(0.5)
+    x[3, :] = -np.inf
+    x[3, 4321] = np.float32(-1e30)
+    for k in (1, 10, 100):
+        v, i = run_select(x, k)
+        assert_select_exact(x, v, i, k)
+
+
+def test_k_equals_v_full_sort():
+    for V in (1, 63, 64, 65, 1000, 2048):
+        x = synthetic.random_logits(2, V, seed=V, ties=10)
+        v, i = run_select(x, V)
+        assert_select_exact(x, v, i, V)
+
+
+def test_all_winners_in_one_chunk_and_ragged_tail():
+    V, k = 32001, 50
+    for C in (1024, 2048):
+        x = synthetic.random_logits(2, V, seed=7)
+        # row 0: every winner inside chunk 7; row 1: every winner in the ragged last chunk
+        x[0, 7 * C: 7 * C + 50] += np.float32(100.0)
+        last = (V - 1) // C * C
+        x[1, last: last + 50] += np.float32(100.0)
+        v, i = run_select(x, k, C)
+        assert_select_exact(x, v, i, k)
+        assert set(i[0]) == set(range(7 * C, 7 * C + 50))
+        assert set(i[1]) == set(range(last, last + 50))
+
+
+def test_k1_is_argmax_and_strided_rows():
+    base = synthetic.random_logits(8, 40000, seed=5, ties=50)
+    t = dev(base)
+    wide = torch.zeros((8, 40960), dtype=torch.float32, device="cuda")
+    wide[:, :40000] = t
+    view = wide[:, :40000]  # row stride 40960 > V
+    v, i = lt.topk_logits(view, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(i.cpu().numpy()[:, 0], np.argmax(base, axis=1))
+    v, i = lt.topk_logits(view, 300)
+    torch.cuda.synchronize()
+    assert_select_exact(base, v.cpu().numpy(), i.cpu().numpy(), 300)
+
+
+@pytest.mark.parametrize("M,k", [(1, 50), (8, 50), (8, 1024), (2, 2048)])
+def test_flagship_vocabulary(M, k):
+    x = synthetic.random_logits(M, 248320, seed=M * 1000 + k)
+    v, i = run_select(x, k)
+    assert_select_exact(x, v, i, k)
+
+
+def test_repeat_bitwise_identical():
+    x = synthetic.random_logits(8, 248320, seed=99, ties=1000)
+    t = dev(x)
+    v0, i0 = lt.topk_logits(t, 50)
+    for _ in range(10):
+        v, i = lt.topk_logits(t, 50)
+        assert torch.equal(i, i0) and torch.equal(v.view(torch.int32), v0.view(torch.int32))
+    assert_select_exact(x, v0.cpu().numpy(), i0.cpu().numpy(), 50)
