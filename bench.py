@@ -251,7 +251,9 @@ def cpu_baseline(args, W, act_q, act_scale, bias):
 def time_calls(hip, stream, call, n, per_step_events):
     """Run n calls back to back behind a GPU spin so host launch cost is hidden.
 
-    Returns (total_ms, [score_ms], [merge_ms])."""
+    With per_step_events the scoring kernel of every call records its own
+    start and end (events attached to its dispatch) and an event after the
+    call closes the merge.  Returns (total_ms, [score_ms], [merge_ms])."""
     import torch
     torch.cuda.synchronize()
     ev0, ev1 = hip.event(), hip.event()
@@ -260,8 +262,7 @@ def time_calls(hip, stream, call, n, per_step_events):
     hip.record(ev0, stream)
     for i in range(n):
         if evs:
-            hip.record(evs[i][0], stream)
-            call(i, evs[i][1])
+            call(i, (evs[i][0], evs[i][1]))
             hip.record(evs[i][2], stream)
         else:
             call(i, None)
@@ -336,7 +337,7 @@ def main():
     d_b = torch.from_numpy(bias).to(dev) if bias is not None else None
     vals = torch.empty((M, k), dtype=torch.float32, device=dev)
     idx = torch.empty((M, k), dtype=torch.int64, device=dev)
-    work = torch.empty(lt.workspace_bytes(M, V, k, args.chunk_rows), dtype=torch.uint8, device=dev)
+    work = lt.new_workspace(M, V, k, args.chunk_rows, device=dev)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s (packed head {lt.packed_bytes(V, H)} B x {args.copies})")
 
@@ -347,7 +348,7 @@ def main():
         wq, ws = copies[i % rot]
         lt.lm_head_topk_binary(d_aq, d_as, wq, ws, bias=d_b, k=k, vocab_size=V,
                                chunk_rows=args.chunk_rows, out=(vals, idx), workspace=work,
-                               score_event=ev)
+                               score_events=ev)
 
     for i in range(args.warmup):
         call(i, None)

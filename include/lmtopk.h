@@ -23,8 +23,9 @@
  *    reported by the HIP runtime while enqueueing maps to LMTOPK_ERR_HIP; a
  *    fault inside a kernel surfaces at the caller's next synchronisation, as
  *    for any asynchronous HIP work.
- *  - The library is stateless and thread safe.  Calls that share a workspace
- *    buffer must be ordered on one stream.
+ *  - The library keeps no state of its own and is thread safe.  A workspace
+ *    needs no initialisation; every call overwrites what it reads.  Calls
+ *    that share a workspace must be ordered on one stream.
  *  - Inputs must be finite or +-inf.  NaN anywhere is outside the contract and
  *    gives an unspecified (but memory-safe) result.
  *  - +0.0 and -0.0 compare equal: they tie and the lower index comes first.
@@ -68,14 +69,16 @@ typedef enum { LMTOPK_F32 = 0, LMTOPK_BF16 = 1 } lmtopk_dtype;
 /* Optional per-call settings; pass NULL for the defaults. */
 typedef struct {
   /* Vocabulary rows per chunk (one workgroup scores and selects one chunk).
-     0 = automatic.  Otherwise a multiple of 64 that is <= 1024, or one of
-     2048 and 4096.  The result never depends on this value. */
+     0 = automatic.  Otherwise a multiple of 64 that is <= 1024, or 2048.
+     The result never depends on this value. */
   int32_t chunk_rows;
   int32_t reserved; /* must be 0 */
-  /* If not NULL: a hipEvent_t (as void*) that is recorded on `stream` right
-     after the chunk-scoring kernel is enqueued, so a caller can time the
-     scoring kernel apart from the merge.  The library does not own it. */
-  void* score_event;
+  /* If not NULL: the address of two hipEvent_t (an array void*[2]).  The
+     chunk-scoring kernel is then launched with hipExtLaunchKernel so that the
+     first event records the kernel's start and the second its end, which
+     times that kernel apart from the merge kernels after it.  The events
+     must exist; the library does not own them. */
+  void* score_events;
 } lmtopk_options;
 
 /* ------------------------------------------------------------------------ */
@@ -113,7 +116,8 @@ typedef struct {
 #define LMTOPK_GROUP_SIZE 128
 #define LMTOPK_MAX_ROWS 8
 #define LMTOPK_MAX_K 2048
-/* Binary path: the per-row activation bit planes live in LDS, M * H bytes. */
+/* Binary path: the activation trit masks of all M rows live in LDS
+   (196 bytes per row and group of 128, about 1.5 * M * H bytes). */
 #define LMTOPK_MAX_BINARY_MH 65536
 
 /* Layout version of packed heads this library reads and writes. */
@@ -130,7 +134,10 @@ lmtopk_status lmtopk_packed_bytes(int64_t V, int64_t H, int32_t group_size,
 
 /* Host-only: workspace bytes needed by lmtopk_binary, lmtopk_dense and
    lmtopk_select for these sizes and options.  The same workspace serves all
-   three.  Errors: NULL, SHAPE, K, OPTIONS. */
+   three.  It holds, per row, the largest logit of every chunk and the chunk
+   candidates (8 bytes each), plus one intermediate merge level when a row
+   has more than 16384 candidates.
+   Errors: NULL, SHAPE, K, OPTIONS. */
 lmtopk_status lmtopk_workspace_bytes(int64_t M, int64_t V, int32_t k,
                                      const lmtopk_options* opt, size_t* bytes);
 

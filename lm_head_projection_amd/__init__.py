@@ -32,6 +32,7 @@ __all__ = [
     "lm_head_topk_dense",
     "topk_logits",
     "library_path",
+    "new_workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,7 +54,7 @@ class LmTopkError(ValueError):
 
 class _Options(ctypes.Structure):
     _fields_ = [("chunk_rows", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("score_event", ctypes.c_void_p)]
+                ("score_events", ctypes.c_void_p)]
 
 
 def _load():
@@ -107,8 +108,16 @@ def packed_bytes(V, H, group_size=GROUP_SIZE):
     return a.value, b.value
 
 
-def _opts(chunk_rows, score_event=None):
-    return _Options(int(chunk_rows), 0, score_event)
+def _opts(chunk_rows, score_events=None):
+    """score_events: None or (start, stop) hipEvent_t handles recorded at the
+    scoring kernel's start and end."""
+    if score_events is None:
+        return _Options(int(chunk_rows), 0, None)
+    start, stop = (e.value if isinstance(e, ctypes.c_void_p) else int(e) for e in score_events)
+    arr = (ctypes.c_void_p * 2)(start, stop)
+    o = _Options(int(chunk_rows), 0, ctypes.cast(arr, ctypes.c_void_p))
+    o._events = arr  # keep the array alive as long as the options
+    return o
 
 
 def workspace_bytes(M, V, k, chunk_rows=0):
@@ -151,10 +160,25 @@ def _outputs(dev, M, k, out):
     return values, indices
 
 
+_WORKSPACES = {}
+
+
+def new_workspace(M, V, k, chunk_rows=0, device=None):
+    """A workspace for these sizes: uint8 on `device` (no initialisation needed)."""
+    return torch.empty(workspace_bytes(M, V, k, chunk_rows), dtype=torch.uint8, device=device)
+
+
 def _workspace(dev, M, V, k, chunk_rows, workspace):
     need = workspace_bytes(M, V, k, chunk_rows)
     if workspace is None:
-        return torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        # one buffer per (device, stream), grown on demand: calls on one
+        # stream are ordered, so they can share it
+        key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+        ws = _WORKSPACES.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            _WORKSPACES[key] = ws
+        return ws
     _need_cuda("workspace", workspace, torch.uint8)
     if workspace.numel() < need:
         raise ValueError(f"workspace needs {need} bytes, got {workspace.numel()}")
@@ -185,7 +209,7 @@ def pack_binary(weight, group_size=GROUP_SIZE):
 
 def lm_head_topk_binary(act_q, act_scale, wq, wscale, bias=None, group_size=GROUP_SIZE, k=50, *,
                         vocab_size=None, chunk_rows=0, out=None, workspace=None,
-                        score_event=None):
+                        score_events=None):
     """Exact top-k of the binary-head logits of each activation row.
 
     act_q int8 [M, H]; act_scale float32 [M]; (wq, wscale) from pack_binary;
@@ -214,7 +238,7 @@ def lm_head_topk_binary(act_q, act_scale, wq, wscale, bias=None, group_size=GROU
     dev = act_q.device
     values, indices = _outputs(dev, M, k, out)
     ws = _workspace(dev, M, V, k, chunk_rows, workspace)
-    o = _opts(chunk_rows, score_event)
+    o = _opts(chunk_rows, score_events)
     _check(_lib.lmtopk_binary(_ptr(act_q), _ptr(act_scale), _ptr(wq), _ptr(wscale), _ptr(bias),
                               M, V, H, group_size, k, _ptr(values), _ptr(indices), _ptr(ws),
                               ws.numel(), ctypes.byref(o), _stream(act_q)))
@@ -222,7 +246,7 @@ def lm_head_topk_binary(act_q, act_scale, wq, wscale, bias=None, group_size=GROU
 
 
 def lm_head_topk_dense(hidden, weight, k=50, bias=None, *, chunk_rows=0, out=None,
-                       workspace=None, score_event=None):
+                       workspace=None, score_events=None):
     """Exact top-k of hidden @ weight.T (+ bias); hidden and weight both fp32 or both bf16."""
     _need_cuda("hidden", hidden, ndim=2)
     _need_cuda("weight", weight, ndim=2)
@@ -239,7 +263,7 @@ def lm_head_topk_dense(hidden, weight, k=50, bias=None, *, chunk_rows=0, out=Non
     dev = hidden.device
     values, indices = _outputs(dev, M, k, out)
     ws = _workspace(dev, M, V, k, chunk_rows, workspace)
-    o = _opts(chunk_rows, score_event)
+    o = _opts(chunk_rows, score_events)
     dt = _BF16 if hidden.dtype == torch.bfloat16 else _F32
     _check(_lib.lmtopk_dense(_ptr(hidden), _ptr(weight), dt, _ptr(bias), M, V, H, k,
                              _ptr(values), _ptr(indices), _ptr(ws), ws.numel(), ctypes.byref(o),
@@ -247,7 +271,7 @@ def lm_head_topk_dense(hidden, weight, k=50, bias=None, *, chunk_rows=0, out=Non
     return values, indices
 
 
-def topk_logits(logits, k, *, chunk_rows=0, out=None, workspace=None, score_event=None):
+def topk_logits(logits, k, *, chunk_rows=0, out=None, workspace=None, score_events=None):
     """The selection stage alone: exact top-k of each row of fp32 logits [M, V]."""
     if not isinstance(logits, torch.Tensor) or logits.device.type != "cuda":
         raise ValueError("logits must be a GPU tensor")
@@ -258,7 +282,7 @@ def topk_logits(logits, k, *, chunk_rows=0, out=None, workspace=None, score_even
     dev = logits.device
     values, indices = _outputs(dev, M, k, out)
     ws = _workspace(dev, M, V, k, chunk_rows, workspace)
-    o = _opts(chunk_rows, score_event)
+    o = _opts(chunk_rows, score_events)
     _check(_lib.lmtopk_select(_ptr(logits), M, V, ld, k, _ptr(values), _ptr(indices), _ptr(ws),
                               ws.numel(), ctypes.byref(o), _stream(logits)))
     return values, indices

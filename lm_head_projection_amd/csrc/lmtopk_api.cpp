@@ -23,7 +23,7 @@ int check_options(const lmtopk_options* opt) {
   if (opt->reserved != 0) return LMTOPK_ERR_OPTIONS;
   const int c = opt->chunk_rows;
   if (c == 0) return LMTOPK_OK;
-  if (c == 2048 || c == 4096) return LMTOPK_OK;
+  if (c == 2048) return LMTOPK_OK;
   if (c >= 64 && c <= 1024 && c % 64 == 0) return LMTOPK_OK;
   return LMTOPK_ERR_OPTIONS;
 }
@@ -53,11 +53,14 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, Geome
     C = V >= 1024 ? 1024 : (int)(g->n_tiles * 64);
   }
   g->chunk_rows = C;
-  g->rpl = C <= 1024 ? 1 : C / 1024;
+  // rows per lane: 1 for chunks of up to 1024 rows (up to 16 waves); a
+  // 2048-row chunk is 8 waves of 4 rows per lane
+  g->rpl = C <= 1024 ? 1 : 4;
   g->nw = C / (64 * g->rpl);
   g->n_chunks = (int)((V + C - 1) / C);
   g->kc = k < C ? k : C;
   const int64_t n0 = (int64_t)g->n_chunks * g->kc;
+  g->maxk_bytes = round_up((size_t)(M * g->n_chunks * 4), 256);
   g->region0_bytes = round_up((size_t)(M * n0 * 8), 256);
 
   // merge plan: a level either fits one workgroup (final) or splits the
@@ -91,7 +94,7 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, Geome
     ++lv;
   }
   g->n_levels = lv;
-  g->workspace_bytes = g->region0_bytes + g->region1_bytes;
+  g->workspace_bytes = g->maxk_bytes + g->region0_bytes + g->region1_bytes;
   return LMTOPK_OK;
 }
 
@@ -171,12 +174,13 @@ static lmtopk_status common_checks(const void* workspace, size_t workspace_bytes
 }
 
 static lmtopk_status finish(const Geometry& g, int e, void* workspace, float* values,
-                            int64_t* indices, const lmtopk_options* opt, void* stream) {
+                            int64_t* indices, void* stream) {
   if (e) return LMTOPK_ERR_HIP;
-  if (opt && opt->score_event) {
-    if (lmtopk::record_event(opt->score_event, stream)) return LMTOPK_ERR_HIP;
-  }
   return lmtopk::hip_status(lmtopk::launch_merges(g, workspace, values, indices, stream));
+}
+
+static void* const* score_events(const lmtopk_options* opt) {
+  return opt ? static_cast<void* const*>(opt->score_events) : nullptr;
 }
 
 lmtopk_status lmtopk_binary(const int8_t* act_q, const float* act_scale, const void* wq,
@@ -197,10 +201,11 @@ lmtopk_status lmtopk_binary(const int8_t* act_q, const float* act_scale, const v
     return LMTOPK_ERR_ALIGN;
   size_t lds_max = 0;
   if (lmtopk::max_lds_per_block(&lds_max)) return LMTOPK_ERR_HIP;
-  if (lmtopk::binary_lds_bytes(M, H) + 8192 > lds_max) return LMTOPK_ERR_SHAPE;
-  const int e = lmtopk::launch_binary_chunks(g, act_q, act_scale, wq, wscale, bias, H, workspace,
-                                             stream);
-  return finish(g, e, workspace, values, indices, opt, stream);
+  if (lmtopk::binary_lds_bytes(M, H) + 32768 > lds_max) return LMTOPK_ERR_SHAPE;
+  const int e =
+      lmtopk::launch_binary_chunks(g, act_q, act_scale, wq, wscale, bias, H, workspace, stream,
+                                   score_events(opt));
+  return finish(g, e, workspace, values, indices, stream);
 }
 
 lmtopk_status lmtopk_dense(const void* hidden, const void* weight, lmtopk_dtype dtype,
@@ -220,10 +225,10 @@ lmtopk_status lmtopk_dense(const void* hidden, const void* weight, lmtopk_dtype 
     return LMTOPK_ERR_ALIGN;
   size_t lds_max = 0;
   if (lmtopk::max_lds_per_block(&lds_max)) return LMTOPK_ERR_HIP;
-  if (lmtopk::dense_lds_bytes(M, g.chunk_rows) + 8192 > lds_max) return LMTOPK_ERR_SHAPE;
+  if (lmtopk::dense_lds_bytes(M, g.chunk_rows) + 32768 > lds_max) return LMTOPK_ERR_SHAPE;
   const int e = lmtopk::launch_dense_chunks(g, hidden, weight, dtype == LMTOPK_BF16, bias, H,
-                                            workspace, stream);
-  return finish(g, e, workspace, values, indices, opt, stream);
+                                            workspace, stream, score_events(opt));
+  return finish(g, e, workspace, values, indices, stream);
 }
 
 lmtopk_status lmtopk_select(const float* logits, int64_t M, int64_t V, int64_t ld, int32_t k,
@@ -236,8 +241,9 @@ lmtopk_status lmtopk_select(const float* logits, int64_t M, int64_t V, int64_t l
   if (st) return st;
   if (ld < V) return LMTOPK_ERR_SHAPE;
   if (!lmtopk::aligned16(logits)) return LMTOPK_ERR_ALIGN;
-  const int e = lmtopk::launch_select_chunks(g, logits, ld, workspace, stream);
-  return finish(g, e, workspace, values, indices, opt, stream);
+  const int e =
+      lmtopk::launch_select_chunks(g, logits, ld, workspace, stream, score_events(opt));
+  return finish(g, e, workspace, values, indices, stream);
 }
 
 }  // extern "C"

@@ -60,25 +60,64 @@ __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }
 
+// Cross-lane steps with DPP (gfx9 row and broadcast controls).  A DPP read of
+// a lane that is out of range, or of a row masked off, yields `old`.
+template <int kCtrl, int kRowMask = 0xF, bool kBoundZero = false>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, kCtrl, kRowMask, 0xF, kBoundZero);
+}
+constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowBcast15 = 0x142;   // lane 15 of a row -> the next row
+constexpr int kRowBcast31 = 0x143;   // lane 31 -> rows 2 and 3
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+
+// Wave-wide min / max / sum; the result is returned to every lane.
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
+  v = min(v, dpp<kQuadSwap1>(0xFFFFFFFFu, v));
+  v = min(v, dpp<kQuadSwap2>(0xFFFFFFFFu, v));
+  v = min(v, dpp<kRowHalfMirror>(0xFFFFFFFFu, v));
+  v = min(v, dpp<kRowMirror>(0xFFFFFFFFu, v));
+  v = min(v, dpp<kRowBcast15, 0xA>(0xFFFFFFFFu, v));
+  v = min(v, dpp<kRowBcast31, 0xC>(0xFFFFFFFFu, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  v = max(v, dpp<kQuadSwap1>(0u, v));
+  v = max(v, dpp<kQuadSwap2>(0u, v));
+  v = max(v, dpp<kRowHalfMirror>(0u, v));
+  v = max(v, dpp<kRowMirror>(0u, v));
+  v = max(v, dpp<kRowBcast15, 0xA>(0u, v));
+  v = max(v, dpp<kRowBcast31, 0xC>(0u, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Inclusive prefix sum over the 16 lanes of each row (Kogge-Stone, zero fill).
+__device__ __forceinline__ uint32_t row_scan_inclusive(uint32_t v) {
+  v += dpp<kRowShr1, 0xF, true>(0u, v);
+  v += dpp<kRowShr2, 0xF, true>(0u, v);
+  v += dpp<kRowShr4, 0xF, true>(0u, v);
+  v += dpp<kRowShr8, 0xF, true>(0u, v);
   return v;
 }
 
-// Inclusive prefix sum over lanes 0..15 (lanes >= 16 get garbage).
-__device__ __forceinline__ uint32_t scan16_inclusive(uint32_t x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    uint32_t t = (uint32_t)__shfl_up((int)x, o);
-    if (lane >= o) x += t;
-  }
-  return x;
+// Inclusive prefix sum over all 64 lanes.
+__device__ __forceinline__ uint32_t wave_scan_inclusive(uint32_t v) {
+  v = row_scan_inclusive(v);
+  v += dpp<kRowBcast15, 0xA>(0u, v);
+  v += dpp<kRowBcast31, 0xC>(0u, v);
+  return v;
+}
+
+// Workgroup barrier that orders LDS only: LDS writes before it are visible to
+// every wave after it, while global loads in flight stay in flight (a full
+// __syncthreads() would also wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // LDS used by one selection (any number of sequential selections may reuse it).
@@ -99,6 +138,7 @@ struct SelectRange {
   uint32_t mask;
   uint32_t need;
   uint32_t total;
+  uint32_t kmax;  // largest valid key (0 if none)
 };
 
 // Block-wide search.  Every thread of the block must call it with its R
@@ -132,25 +172,20 @@ __device__ SelectRange block_select(const uint32_t (&key)[R], uint32_t valid, ui
     sm.wmax[wave] = lmax;
     sm.wcnt[wave] = cnt;
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t a = 0xFFFFFFFFu, b = 0u, c = 0u;
   if (lane < nw) {
     a = sm.wmin[lane];
     b = sm.wmax[lane];
     c = sm.wcnt[lane];
   }
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) {
-    a = min(a, (uint32_t)__shfl_xor((int)a, o));
-    b = max(b, (uint32_t)__shfl_xor((int)b, o));
-    c += (uint32_t)__shfl_xor((int)c, o);
-  }
-  const uint32_t gmin = readlane_u32(a, 0);
-  const uint32_t gmax = readlane_u32(b, 0);
-  const uint32_t total = readlane_u32(c, 0);
+  const uint32_t gmin = wave_min_u32(a);
+  const uint32_t gmax = wave_max_u32(b);
+  const uint32_t total = readlane_u32(row_scan_inclusive(c), 15);
 
   SelectRange res;
   res.total = total;
+  res.kmax = total ? gmax : 0u;
   if (total <= k) {  // every valid entry is selected
     res.prefix = 0u;
     res.mask = 0u;
@@ -178,17 +213,12 @@ __device__ SelectRange block_select(const uint32_t (&key)[R], uint32_t valid, ui
       if (((valid >> r) & 1u) && ((key[r] & mask) == prefix))
         atomicAdd(&hist[(key[r] >> shift) & dmask], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     // every wave finds the digit of the k-th key on its own
     const uint4 h = *reinterpret_cast<const uint4*>(&hist[4 * lane]);
     const uint32_t s3 = h.w, s2 = h.z + s3, s1 = h.y + s2, s0 = h.x + s1;
-    uint32_t x = s0;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t t = (uint32_t)__shfl_down((int)x, o);
-      if (lane + o < 64) x += t;
-    }
-    const uint32_t after = x - s0;  // keys in lanes above this one
+    const uint32_t incl = wave_scan_inclusive(s0);
+    const uint32_t after = readlane_u32(incl, 63) - incl;  // keys in lanes above this one
     const uint64_t have = ballot(s0 + after >= need);
     const int L = 63 - __clzll(have);
     uint32_t ge_i, h_i;
@@ -244,18 +274,18 @@ __device__ uint32_t block_compact(const uint32_t (&key)[R], uint32_t valid, cons
     sm.cgt[wave] = ngt;
     sm.ceq[wave] = neq;
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t cg = 0, ce = 0;
   if (lane < nw) {
     cg = sm.cgt[lane];
     ce = sm.ceq[lane];
   }
-  const uint32_t ce_incl = scan16_inclusive(ce, lane);
+  const uint32_t ce_incl = row_scan_inclusive(ce);
   const uint32_t ce_excl = ce_incl - ce;
   const uint32_t left = s.need > ce_excl ? s.need - ce_excl : 0u;
   const uint32_t take = lane < nw ? min(ce, left) : 0u;
   const uint32_t sel = cg + take;
-  const uint32_t sel_incl = scan16_inclusive(sel, lane);
+  const uint32_t sel_incl = row_scan_inclusive(sel);
   uint32_t eq_before = readlane_u32(ce_excl, wave);
   uint32_t sel_before = readlane_u32(sel_incl - sel, wave);
   const uint32_t selected = readlane_u32(sel_incl, nw - 1);
@@ -270,6 +300,224 @@ __device__ uint32_t block_compact(const uint32_t (&key)[R], uint32_t valid, cons
     sel_before += (uint32_t)__popcll(bsel);
   }
   return selected;
+}
+
+// LDS of the final merge: up to kMaxK entries to sort (4 slack entries so the
+// rank loop can read whole uint4 words), their ranks, and two scalars.
+struct alignas(16) FinalSmem {
+  uint32_t key[kMaxK + 4];
+  uint32_t bits[kMaxK + 4];
+  int32_t idx[kMaxK + 4];
+  uint32_t rank[kMaxK + 4];
+  uint32_t count;  // survivors placed so far
+  uint32_t bound;  // survivor threshold (a key)
+};
+
+// Entries [0, n) of fs are filled, [n, 4 * ceil(n / 4)) hold padding that is
+// never ahead of anything, and rank[0, n) is zero.  Each entry's output
+// position is the number of entries ahead of it (greater key, or equal key
+// and lower index).  The count for entry i is split over up to
+// blockDim / n threads, each scanning one segment of the entries, and summed
+// with LDS atomics (integer adds: the result does not depend on their order).
+__device__ void rank_and_write(FinalSmem& fs, uint32_t n, uint32_t k, float* values,
+                               int64_t* indices) {
+  if (n == 0) return;
+  const uint32_t nq = (n + 3u) >> 2;
+  uint32_t segs = blockDim.x / n;
+  segs = segs < 1u ? 1u : (segs > nq ? nq : segs);
+  const uint32_t per = (nq + segs - 1u) / segs;
+  for (uint32_t t = threadIdx.x; t < n * segs; t += blockDim.x) {
+    const uint32_t i = t % n;
+    const uint32_t q0 = (t / n) * per;
+    const uint32_t q1 = min(nq, q0 + per);
+    const uint32_t ki = fs.key[i];
+    const int32_t ii = fs.idx[i];
+    uint32_t rank = 0;
+    for (uint32_t q = q0; q < q1; ++q) {
+      const uint4 kj = *reinterpret_cast<const uint4*>(&fs.key[4 * q]);
+      const int4 ij = *reinterpret_cast<const int4*>(&fs.idx[4 * q]);
+      rank += (kj.x > ki || (kj.x == ki && ij.x < ii)) ? 1u : 0u;
+      rank += (kj.y > ki || (kj.y == ki && ij.y < ii)) ? 1u : 0u;
+      rank += (kj.z > ki || (kj.z == ki && ij.z < ii)) ? 1u : 0u;
+      rank += (kj.w > ki || (kj.w == ki && ij.w < ii)) ? 1u : 0u;
+    }
+    if (rank) atomicAdd(&fs.rank[i], rank);
+  }
+  lds_barrier();
+  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint32_t rank = fs.rank[i];
+    if (rank < k) {
+      values[rank] = __uint_as_float(fs.bits[i]);
+      indices[rank] = (int64_t)fs.idx[i];
+    }
+  }
+}
+
+// Survivor threshold from the chunk maxima held by one wave (m[r] of lane l is
+// chunk r * 64 + l; chunks >= n_max are absent; k <= n_max <= 256).  Returns a
+// key T such that at least k of the maxima are >= T, so T is at most the k-th
+// largest maximum.  MSB-first search for the k-th largest, one bit per step
+// below the bits all maxima share; it stops as soon as the keys that share
+// the prefix found so far are exactly the ones still needed, or once bit
+// kBoundLowBit is decided (a coarser T only lets a few more candidates pass).
+constexpr int kBoundLowBit = 16;
+
+__device__ __forceinline__ uint32_t wave_bound(uint32_t (&m)[4], int n_max, uint32_t k) {
+  const int lane = lane_id();
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (r * 64 + lane < n_max) {
+      lo = min(lo, m[r]);
+      hi = max(hi, m[r]);
+    }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lo == hi) return lo;
+  // absent chunks become copies of the smallest maximum: with k <= n_max
+  // that leaves every bound >= lo unchanged, and any T <= lo is valid anyway
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (r * 64 + lane >= n_max) m[r] = lo;
+  const int common = __clz(lo ^ hi);
+  uint32_t mask = common ? (0xFFFFFFFFu << (32 - common)) : 0u;
+  uint32_t prefix = hi & mask;
+  uint32_t need = k;      // keys still needed from the current range
+  uint32_t inside = 256;  // keys in the current range
+  for (int bit = 31 - common; bit >= kBoundLowBit; --bit) {
+    const uint32_t mb = mask | (1u << bit);
+    const uint32_t pb = prefix | (1u << bit);
+    uint32_t upper = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) upper += (uint32_t)__popcll(ballot((m[r] & mb) == pb));
+    if (upper >= need) {
+      prefix = pb;
+      inside = upper;
+    } else {
+      need -= upper;
+      inside -= upper;
+    }
+    mask = mb;
+    if (inside == need) break;
+  }
+  return prefix;
+}
+
+// Final merge of one row.  `in` holds n_in candidates (fp32 value bits, int32
+// index) in ascending index order, index -1 = padding; RM slots per thread
+// cover them (n_in <= blockDim.x * RM).  `maxk` (optional) holds the largest
+// key of each of the n_max chunks the candidates came from.  Writes the exact
+// top-k sorted by (value desc, index asc).
+//
+// Bounded path: a threshold T with at least k chunk maxima >= T is at most
+// the row's k-th largest value (those maxima are k distinct logits), so only
+// candidates with key >= T can be in the result.  Wave 0 finds T while the
+// candidate loads of every wave are still in flight; the survivors (typically
+// a few dozen) go to LDS in any order and are ranked there.  When there are
+// too many chunks or survivors, the radix select of all candidates runs
+// instead.
+constexpr uint32_t kSurvivorsMax = 512;
+
+template <int RM>
+__device__ void merge_final(const uint2* in, int64_t n_in, const uint32_t* maxk, int n_max,
+                            uint32_t k, float* values, int64_t* indices, int nthreads,
+                            SelectSmem& sm, FinalSmem& fs) {
+  // nthreads == blockDim.x, passed in so that no load of it queues behind
+  // the candidate loads
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const bool bounded = maxk != nullptr && n_max >= (int)k && n_max <= 256;
+
+  // Every load is unconditional (addresses clamped into the arrays, the
+  // extra entries marked invalid) so that all of them are in flight at once.
+  uint32_t m[4] = {0u, 0u, 0u, 0u};
+  if (bounded && wave == 0) {  // issued first: the bound only waits for these
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = maxk[min(r * 64 + lane, n_max - 1)];
+  }
+  uint32_t key[RM], vb[RM];
+  int32_t idx[RM];
+  uint32_t inside = 0u;  // slots that lie in [0, n_in); known before the loads land
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    const int64_t pos = (int64_t)(wave * RM + r) * 64 + lane;
+    const uint2 e = in[pos < n_in ? pos : n_in - 1];
+    vb[r] = e.x;
+    idx[r] = (int32_t)e.y;
+    inside |= (pos < n_in ? 1u : 0u) << r;
+  }
+  for (int i = tid; i < kMaxK + 4; i += nthreads) fs.rank[i] = 0u;
+
+  if (bounded) {
+    for (int i = tid; i < (int)kSurvivorsMax + 4; i += nthreads) {
+      fs.key[i] = 0u;  // padding: below every real key
+      fs.idx[i] = 0x7FFFFFFF;
+    }
+    if (wave == 0) {
+      const uint32_t t = wave_bound(m, n_max, k);
+      if (lane == 0) {
+        fs.bound = t;
+        fs.count = 0u;
+      }
+    }
+    lds_barrier();
+  }
+  // keys and validity only now, so that wave 0 found the bound without
+  // waiting for its candidate loads
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    key[r] = float_key(__uint_as_float(vb[r]));
+    valid |= (((inside >> r) & 1u) && idx[r] >= 0 ? 1u : 0u) << r;
+  }
+  if (bounded) {
+    const uint32_t t = fs.bound;
+    // survivors of this wave go to a block of slots reserved with one atomic
+    uint64_t sv[RM];
+    uint32_t nsv = 0;
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      sv[r] = ballot(((valid >> r) & 1u) && key[r] >= t);
+      nsv += (uint32_t)__popcll(sv[r]);
+    }
+    if (nsv) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&fs.count, nsv);
+      base = readlane_u32(base, 0);
+#pragma unroll
+      for (int r = 0; r < RM; ++r) {
+        const uint32_t p = base + lanes_below(sv[r]);
+        if (((sv[r] >> lane) & 1u) && p < kSurvivorsMax) {
+          fs.key[p] = key[r];
+          fs.bits[p] = vb[r];
+          fs.idx[p] = idx[r];
+        }
+        base += (uint32_t)__popcll(sv[r]);
+      }
+    }
+    lds_barrier();
+    const uint32_t n = fs.count;
+    if (n <= kSurvivorsMax) {
+      rank_and_write(fs, n, k, values, indices);
+      return;
+    }
+  }
+
+  const SelectRange s = block_select<RM>(key, valid, k, sm);
+  const uint32_t n = block_compact<RM>(key, valid, s, vb, idx, sm,
+                                       [&](uint32_t pos, uint32_t bits, int32_t ix) {
+                                         fs.key[pos] = float_key(__uint_as_float(bits));
+                                         fs.bits[pos] = bits;
+                                         fs.idx[pos] = ix;
+                                       });
+  for (uint32_t i = n + tid; i < ((n + 3u) & ~3u); i += blockDim.x) {
+    fs.key[i] = 0u;
+    fs.idx[i] = 0x7FFFFFFF;
+  }
+  lds_barrier();
+  rank_and_write(fs, n, k, values, indices);
 }
 
 }  // namespace lmtopk

@@ -28,8 +28,9 @@ struct Geometry {
   int n_chunks;
   int kc;          // candidate slots per chunk per row = min(k, C)
   int64_t n_tiles; // 64-row tiles covering V
-  int n_levels;
+  int n_levels;    // merge kernel launches
   MergeLevel level[kMaxMergeLevels];
+  size_t maxk_bytes;     // largest key of each chunk [M][n_chunks] x 4 B
   size_t region0_bytes;  // chunk candidates [M][n_chunks * kc] x 8 B
   size_t region1_bytes;  // first intermediate merge output, or 0
   size_t workspace_bytes;
@@ -38,19 +39,20 @@ struct Geometry {
 // Returns 0 or an lmtopk_status code (SHAPE, K, OPTIONS).
 int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, Geometry* g);
 
-// Launchers; each returns a hipError_t value (0 = success).
+// Launchers; each returns a hipError_t value (0 = success).  `events` of the
+// chunk launchers: null, or two hipEvent_t recording the kernel's start and end.
 int launch_pack(const void* w, int w_is_bf16, int64_t V, int64_t H, void* wq, float* wscale,
                 void* stream);
 int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* act_scale,
                          const void* wq, const float* wscale, const float* bias, int64_t H,
-                         void* workspace, void* stream);
+                         void* workspace, void* stream, void* const* events);
 int launch_dense_chunks(const Geometry& g, const void* hidden, const void* weight, int is_bf16,
-                        const float* bias, int64_t H, void* workspace, void* stream);
+                        const float* bias, int64_t H, void* workspace, void* stream,
+                        void* const* events);
 int launch_select_chunks(const Geometry& g, const float* logits, int64_t ld, void* workspace,
-                         void* stream);
+                         void* stream, void* const* events);
 int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* indices,
                   void* stream);
-int record_event(void* event, void* stream);
 // Largest LDS (bytes) one workgroup may use on the current device.
 int max_lds_per_block(size_t* bytes);
 

@@ -19,6 +19,7 @@
 // "lower index first" on ties reduces to "earlier position first".
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "lmtopk_device.hpp"
@@ -99,7 +100,8 @@ __global__ __launch_bounds__(256) void k_pack(const void* __restrict__ w, int64_
 // shared pieces of the chunk kernels
 // ---------------------------------------------------------------------------
 struct ChunkOut {
-  uint2* cand;   // [M][n_chunks][kc]
+  uint2* cand;      // [M][n_chunks][kc]
+  uint32_t* maxk;   // [M][n_chunks] largest key of each chunk
   int n_chunks;
   int kc;
   int k;
@@ -118,6 +120,7 @@ __device__ __forceinline__ void chunk_select_write(const float (&val)[RPL], cons
     key[r] = float_key(val[r]);
   }
   const SelectRange s = block_select<RPL>(key, valid, (uint32_t)o.k, sm);
+  if (threadIdx.x == 0) o.maxk[(size_t)m * o.n_chunks + blockIdx.x] = s.kmax;
   uint2* out = o.cand + ((size_t)m * o.n_chunks + blockIdx.x) * o.kc;
   const uint32_t n = block_compact<RPL>(key, valid, s, vb, idx, sm,
                                         [&](uint32_t pos, uint32_t bits, int32_t ix) {
@@ -130,6 +133,21 @@ __device__ __forceinline__ void chunk_select_write(const float (&val)[RPL], cons
 // ---------------------------------------------------------------------------
 // binary chunk kernel
 // ---------------------------------------------------------------------------
+// Activations in balanced ternary.  Every int8 activation a is written as
+// a = sum_{p<6} 3^p d_p with digits d_p in {-1, 0, +1} (six trits reach
+// +-364).  For one group of 128 activations and trit p, two bit masks are
+// kept: NZ_p (d_p != 0) and POS_p (d_p == +1).  With the sign bits b of one
+// weight row (bit 1 = +1) the group's trit-p dot is
+//   sum_j sign_j d_pj = 2 popcount(XNOR(b, POS_p) AND NZ_p) - popcount(NZ_p),
+// so the exact integer group dot is
+//   D = sum_j a_j sign_j = 2 S - C,   S = sum_p 3^p popcount(XNOR(b, POS_p) AND NZ_p),
+//   C = sum_p 3^p popcount(NZ_p)  (the same for every weight row).
+// Per 32 weights and trit that is one 3-input bit operation (v_bitop3) and
+// one accumulating popcount (v_bcnt), 48 + 5 Horner steps per group of 128.
+struct TritGroup {
+  uint4 pos_nz[12];  // [trit p] -> {POS_p, NZ_p}, 4 words = 128 activations each
+};
+
 struct BinaryArgs {
   const int8_t* act_q;     // [M][H]
   const float* act_scale;  // [M]
@@ -142,144 +160,261 @@ struct BinaryArgs {
   ChunkOut out;
 };
 
-__device__ __forceinline__ uint32_t and_popc4(const uint4& w, const uint4& p) {
-  return __popc(w.x & p.x) + __popc(w.y & p.y) + __popc(w.z & p.z) + __popc(w.w & p.w);
+__device__ __forceinline__ uint32_t bcnt_acc(uint32_t x, uint32_t acc) {
+  uint32_t r;
+  asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(acc));
+  return r;
 }
 
 __device__ __forceinline__ float comp4(const float4& f, int i) {
   return i == 0 ? f.x : i == 1 ? f.y : i == 2 ? f.z : f.w;
 }
 
-// Lane r of wave w owns rows ((chunk * tiles_per_chunk + w * RPL + s) * 64 + r)
-// for s < RPL.  Per group g of 128 weights the lane loads one uint4 of sign
-// bits per row; per row m of activations, the group's exact integer dot is
-//   D = sum_j a_j * sign_j = 2 * S - A,  S = sum_j [bit_j] a_j,  A = sum_j a_j,
-// with S built from the 8 two's-complement bit planes of the activations:
-//   S = -128 * c_7 + sum_{p<7} 2^p * c_p,   c_p = popcount(bits AND plane_p),
-// and the fp32 logit accumulates fmaf((float)D, scale_g, acc) in ascending g.
-template <int M, int RPL>
-__global__ __launch_bounds__(1024) void k_binary_chunk(BinaryArgs a) {
+// S of one group for R weight rows at once: the trit masks are read once and
+// serve all R rows.
+template <int R>
+__device__ __forceinline__ void trit_dot(const uint4 (&w)[R], const uint4* tg, uint32_t (&u)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) u[r] = 0u;
+#pragma unroll
+  for (int p = 5; p >= 0; --p) {
+    const uint4 pos = tg[2 * p];
+    const uint4 nz = tg[2 * p + 1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t x = (u[r] << 1) + u[r];
+      x = bcnt_acc(~(w[r].x ^ pos.x) & nz.x, x);
+      x = bcnt_acc(~(w[r].y ^ pos.y) & nz.y, x);
+      x = bcnt_acc(~(w[r].z ^ pos.z) & nz.z, x);
+      x = bcnt_acc(~(w[r].w ^ pos.w) & nz.w, x);
+      u[r] = x;
+    }
+  }
+}
+
+// Lane l of wave w owns the R rows ((chunk * tiles_per_chunk + w * R + r) * 64 + l),
+// r < R, and scores them together.  Each group's 128 sign bits of a row are
+// one 16-byte load; the four scales of a quad of groups are one more.  The
+// fp32 logit accumulates fmaf((float)D_g, scale_g, acc) in ascending g, so
+// every row takes the same operation sequence wherever it sits.
+//
+// Latency: the activation bytes are requested first and the first two quads
+// of weights right after them; the trit masks are built while those weights
+// are in flight (the barriers here only order LDS, so they do not wait for
+// the weight loads).  In the steady state two quads are in flight while one
+// is computed; the loads are issued unconditionally and pinned in place so
+// that each wait covers only the buffer about to be used.
+template <int M, int R>
+__global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs a) {
   extern __shared__ __align__(16) uint8_t dyn_lds[];
   __shared__ SelectSmem ssm;
   const int G = a.G;
-  uint4* planes = reinterpret_cast<uint4*>(dyn_lds);          // [M][G][8]
-  int* neg_a = reinterpret_cast<int*>(planes + (size_t)M * G * 8);  // [M][G]
+  uint16_t* table = reinterpret_cast<uint16_t*>(dyn_lds);             // [256] trit codes
+  TritGroup* tgs = reinterpret_cast<TritGroup*>(dyn_lds + 512);       // [M][G]
+  int* cg = reinterpret_cast<int*>(tgs + (size_t)M * G);              // [M][G] C of the group
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
   const int nw = blockDim.x >> 6;
+  const int Qf = G >> 2;  // full quads
+  const int64_t tile0 = (int64_t)blockIdx.x * a.tiles_per_chunk + (int64_t)wave * R;
+  const bool active = tile0 < a.n_tiles;
 
-  // activation bit planes: for 64 consecutive activations, bit p of every
-  // lane's value is one ballot = two plane words
-  for (int mg = wave; mg < M * G; mg += nw) {
-    const int m = mg / G;
-    const int g = mg - m * G;
-    const int8_t* src = a.act_q + (size_t)m * a.H + (size_t)g * kGroup;
-    const int a0 = src[lane];
-    const int a1 = src[64 + lane];
-    uint4 mine = make_uint4(0u, 0u, 0u, 0u);
+  // a tile past the last one reads the last tile; its rows are never offered
+  const uint4* wp[R];
+  const float4* sp[R];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const uint64_t b0 = ballot((a0 >> p) & 1);
-      const uint64_t b1 = ballot((a1 >> p) & 1);
-      if (lane == p)
-        mine = make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1, (uint32_t)(b1 >> 32));
-    }
-    if (lane < 8) planes[((size_t)m * G + g) * 8 + lane] = mine;
-    int s = a0 + a1;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
-    if (lane == 0) neg_a[m * G + g] = -s;
+  for (int r = 0; r < R; ++r) {
+    const int64_t t = tile0 + r < a.n_tiles ? tile0 + r : a.n_tiles - 1;
+    wp[r] = a.wq + (size_t)t * G * 64 + lane;
+    sp[r] = a.wscale + (size_t)t * a.Q * 64 + lane;
   }
-  __syncthreads();
 
-  const int64_t tile0 = (int64_t)blockIdx.x * a.tiles_per_chunk + (int64_t)wave * RPL;
-  bool ok[RPL];
+  // Prologue.  Everything whose load count depends on the shapes happens
+  // before the weight prefetch, and the prefetch is followed only by
+  // straight-line code, so the waits after it cover exactly what they need.
+  // 1. trit code of every int8 value: bits 0..5 NZ_p, bits 8..13 POS_p
+  for (int e = tid; e < 256; e += blockDim.x) {
+    int v = e < 128 ? e : e - 256;
+    uint32_t c = 0u;
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) ok[r] = (tile0 + r) < a.n_tiles;
+    for (int p = 0; p < 6; ++p) {
+      int r = v % 3;  // in {-2, ..., 2}
+      if (r == 2) r = -1;
+      if (r == -2) r = 1;
+      if (r != 0) c |= 1u << p;
+      if (r == 1) c |= 1u << (8 + p);
+      v = (v - r) / 3;
+    }
+    table[e] = (uint16_t)c;
+  }
+  lds_barrier();
 
-  float acc[RPL][M];
+  // 2. trit masks of a batch of groups: each mask word is one ballot over 64
+  //    activations (groups b0, b0 + nw, ..., this wave's share)
+  constexpr int kBatch = 4;
+  const int n_mg = M * G;
+  auto load_acts = [&](int b0, int8_t (&y0)[kBatch], int8_t (&y1)[kBatch]) {
 #pragma unroll
-  for (int r = 0; r < RPL; ++r)
+    for (int i = 0; i < kBatch; ++i) {
+      int mg = b0 + i * nw;
+      mg = mg < n_mg ? mg : n_mg - 1;  // clamped; the extra groups are not used
+      const int m = mg / G;
+      const int8_t* src = a.act_q + (size_t)m * a.H + (size_t)(mg - m * G) * kGroup;
+      y0[i] = src[lane];
+      y1[i] = src[64 + lane];
+    }
+  };
+  auto build_masks = [&](int b0, const int8_t (&y0)[kBatch], const int8_t (&y1)[kBatch]) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int mg = b0 + i * nw;
+      if (mg >= n_mg) break;
+      const uint32_t c0 = table[(uint8_t)y0[i]];
+      const uint32_t c1 = table[(uint8_t)y1[i]];
+      uint4 mine = make_uint4(0u, 0u, 0u, 0u);
+      int cgroup = 0, w3 = 1;
+#pragma unroll
+      for (int p = 0; p < 6; ++p) {
+        const uint64_t p0 = ballot((c0 >> (8 + p)) & 1u), p1 = ballot((c1 >> (8 + p)) & 1u);
+        const uint64_t n0 = ballot((c0 >> p) & 1u), n1 = ballot((c1 >> p) & 1u);
+        if (lane == 2 * p)
+          mine = make_uint4((uint32_t)p0, (uint32_t)(p0 >> 32), (uint32_t)p1, (uint32_t)(p1 >> 32));
+        if (lane == 2 * p + 1)
+          mine = make_uint4((uint32_t)n0, (uint32_t)(n0 >> 32), (uint32_t)n1, (uint32_t)(n1 >> 32));
+        cgroup += w3 * (__popcll(n0) + __popcll(n1));
+        w3 *= 3;
+      }
+      if (lane < 12) tgs[mg].pos_nz[lane] = mine;
+      if (lane == 0) cg[mg] = cgroup;
+    }
+  };
+  //    batches after the first (large M * H only)
+  for (int b0 = wave + nw * kBatch; b0 < n_mg; b0 += nw * kBatch) {
+    int8_t y0[kBatch], y1[kBatch];
+    load_acts(b0, y0, y1);
+    build_masks(b0, y0, y1);
+  }
+  // 3. the first batch's activation bytes
+  int8_t x0[kBatch], x1[kBatch];
+  load_acts(wave, x0, x1);
+  __builtin_amdgcn_sched_barrier(0);  // the activation loads stay ahead of the weight loads
+
+  // 4. first two quads of weights (group and quad indices clamped into the head)
+  //    (issued in the same order as the main loop's refills: all of quad 0,
+  //    then all of quad 1)
+  uint4 bufA[R][4], bufB[R][4];
+  float4 sA[R], sB[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    sA[r] = sp[r][0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bufA[r][i] = wp[r][(i < G ? i : G - 1) * 64];
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    sB[r] = sp[r][(a.Q > 1 ? 1 : 0) * 64];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bufB[r][i] = wp[r][(4 + i < G ? 4 + i : G - 1) * 64];
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  // 5. the first batch's masks, built while the weights are in flight
+  build_masks(wave, x0, x1);
+  lds_barrier();
+
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
 
-  uint4 wc[4][RPL];
-  float4 sc[RPL];
-  auto load_quad = [&](int q, uint4 (&w)[4][RPL], float4 (&s)[RPL]) {
+  auto compute_group = [&](int g, const uint4 (&w)[R], const float (&s)[R]) {
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-      s[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int m = 0; m < M; ++m) {
+      uint32_t u[R];
+      trit_dot<R>(w, tgs[(size_t)m * G + g].pos_nz, u);
+      const int c = cg[m * G + g];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i][r] = make_uint4(0u, 0u, 0u, 0u);
-      if (ok[r]) {
-        const int64_t t = tile0 + r;
-        s[r] = a.wscale[((size_t)t * a.Q + q) * 64 + lane];
+      for (int r = 0; r < R; ++r) acc[r][m] = fmaf((float)(2 * (int)u[r] - c), s[r], acc[r][m]);
+    }
+  };
+  auto compute_quad = [&](int q, const uint4 (&buf)[R][4], const float4 (&s)[R]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int g = 4 * q + i;
-          if (g < G) w[i][r] = a.wq[((size_t)t * G + g) * 64 + lane];
-        }
+    for (int i = 0; i < 4; ++i) {
+      uint4 w[R];
+      float sc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        w[r] = buf[r][i];
+        sc[r] = comp4(s[r], i);
       }
+      compute_group(4 * q + i, w, sc);
+    }
+  };
+  auto load_quad = [&](int q, uint4 (&w)[R][4], float4 (&s)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      s[r] = sp[r][q * 64];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[r][i] = wp[r][(4 * q + i) * 64];
     }
   };
 
-  load_quad(0, wc, sc);
-  for (int q = 0; q < a.Q; ++q) {
-    uint4 wn[4][RPL];
-    float4 sn[RPL];
-    if (q + 1 < a.Q) load_quad(q + 1, wn, sn);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = 4 * q + i;
-      if (g < G) {
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const uint4* P = planes + ((size_t)m * G + g) * 8;
-          uint4 pl[8];
-#pragma unroll
-          for (int p = 0; p < 8; ++p) pl[p] = P[p];
-          const int na = neg_a[m * G + g];
-#pragma unroll
-          for (int r = 0; r < RPL; ++r) {
-            const uint4 w = wc[i][r];
-            int S = -(int)and_popc4(w, pl[7]);
-#pragma unroll
-            for (int p = 6; p >= 0; --p) S = 2 * S + (int)and_popc4(w, pl[p]);
-            const int D = 2 * S + na;
-            acc[r][m] = fmaf((float)D, comp4(sc[r], i), acc[r][m]);
-          }
-        }
-      }
+  if (active) {
+    // quads q (buffer A) and q + 1 (buffer B) are in flight at the top
+    int q = 0;
+    for (; q + 3 < Qf; q += 2) {
+      compute_quad(q, bufA, sA);
+      __builtin_amdgcn_sched_barrier(0);  // keep each refill right after its buffer's last use
+      load_quad(q + 2, bufA, sA);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_quad(q + 1, bufB, sB);
+      __builtin_amdgcn_sched_barrier(0);
+      load_quad(q + 3, bufB, sB);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (q + 1 < a.Q) {
+    if (q < Qf) {
+      compute_quad(q, bufA, sA);
+      if (q + 2 < Qf) load_quad(q + 2, bufA, sA);
+    }
+    if (q + 1 < Qf) compute_quad(q + 1, bufB, sB);
+    if (q + 2 < Qf) compute_quad(q + 2, bufA, sA);
+    if (4 * Qf < G) {  // last, partial quad
+      float4 st[R];
 #pragma unroll
-      for (int r = 0; r < RPL; ++r) {
-        sc[r] = sn[r];
+      for (int r = 0; r < R; ++r) st[r] = sp[r][Qf * 64];
+      for (int g = 4 * Qf; g < G; ++g) {
+        uint4 w[R];
+        float sc[R];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wc[i][r] = wn[i][r];
+        for (int r = 0; r < R; ++r) {
+          w[r] = wp[r][g * 64];
+          sc[r] = comp4(st[r], g - 4 * Qf);
+        }
+        compute_group(g, w, sc);
       }
     }
   }
 
-  int32_t idx[RPL];
+  int32_t idx[R];
   uint32_t valid = 0u;
-  float bias_v[RPL];
+  float bias_v[R];
 #pragma unroll
-  for (int r = 0; r < RPL; ++r) {
+  for (int r = 0; r < R; ++r) {
     const int64_t v = (tile0 + r) * 64 + lane;
     idx[r] = (int32_t)v;
-    const bool vv = ok[r] && v < a.V;
+    const bool vv = (tile0 + r) < a.n_tiles && v < a.V;
     valid |= (vv ? 1u : 0u) << r;
     bias_v[r] = (a.bias != nullptr && vv) ? a.bias[v] : 0.f;
   }
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const float s = a.act_scale[m];
-    float val[RPL];
+    float val[R];
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) val[r] = fmaf(acc[r][m], s, bias_v[r]);
-    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm);
+    for (int r = 0; r < R; ++r) val[r] = fmaf(acc[r][m], s, bias_v[r]);
+    chunk_select_write<R>(val, idx, valid, m, a.out, ssm);
   }
 }
 
@@ -428,8 +563,11 @@ __global__ __launch_bounds__(1024) void k_select_chunk(SelectArgs a) {
 // ---------------------------------------------------------------------------
 struct MergeArgs {
   const uint2* in;  // [M][n_in] candidates, ascending index within each row
+  const uint32_t* maxk;  // [M][n_max] chunk maxima for the bound, or null
+  int n_max;
   int64_t n_in;
   int k;
+  int threads;      // blockDim.x
   int n_seg;        // segments per row; blockIdx.x = segment, blockIdx.y = row
   int64_t seg;      // candidates per segment
   uint2* out;       // intermediate: [M][n_seg][k]
@@ -446,14 +584,18 @@ struct MergeArgs {
 template <int RM>
 __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
   __shared__ SelectSmem ssm;
-  __shared__ uint32_t f_key[kMaxK];
-  __shared__ uint32_t f_bits[kMaxK];
-  __shared__ int32_t f_idx[kMaxK];
+  const int m = blockIdx.y;
+  const uint2* in = a.in + (size_t)m * a.n_in;
+  if (a.n_seg == 1) {
+    __shared__ FinalSmem fs;
+    merge_final<RM>(in, a.n_in, a.maxk ? a.maxk + (size_t)m * a.n_max : nullptr, a.n_max,
+                    (uint32_t)a.k, a.values + (size_t)m * a.k, a.indices + (size_t)m * a.k,
+                    a.threads, ssm, fs);
+    return;
+  }
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
-  const int m = blockIdx.y;
   const int64_t s0 = (int64_t)blockIdx.x * a.seg;
-  const uint2* in = a.in + (size_t)m * a.n_in;
   uint32_t key[RM], vb[RM];
   int32_t idx[RM];
   uint32_t valid = 0u;
@@ -469,36 +611,13 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
     valid |= (idx[r] >= 0 ? 1u : 0u) << r;
   }
   const SelectRange s = block_select<RM>(key, valid, (uint32_t)a.k, ssm);
-  if (a.n_seg > 1) {
-    uint2* out = a.out + ((size_t)m * a.n_seg + blockIdx.x) * a.k;
-    const uint32_t n = block_compact<RM>(key, valid, s, vb, idx, ssm,
-                                         [&](uint32_t pos, uint32_t bits, int32_t ix) {
-                                           out[pos] = make_uint2(bits, (uint32_t)ix);
-                                         });
-    for (int i = (int)n + (int)threadIdx.x; i < a.k; i += blockDim.x)
-      out[i] = make_uint2(0u, 0xFFFFFFFFu);
-    return;
-  }
+  uint2* out = a.out + ((size_t)m * a.n_seg + blockIdx.x) * a.k;
   const uint32_t n = block_compact<RM>(key, valid, s, vb, idx, ssm,
                                        [&](uint32_t pos, uint32_t bits, int32_t ix) {
-                                         f_key[pos] = float_key(__uint_as_float(bits));
-                                         f_bits[pos] = bits;
-                                         f_idx[pos] = ix;
+                                         out[pos] = make_uint2(bits, (uint32_t)ix);
                                        });
-  __syncthreads();
-  for (uint32_t i = threadIdx.x; i < n; i += blockDim.x) {
-    const uint32_t ki = f_key[i];
-    const int32_t ii = f_idx[i];
-    uint32_t rank = 0;
-    for (uint32_t j = 0; j < n; ++j) {
-      const uint32_t kj = f_key[j];
-      rank += (kj > ki || (kj == ki && f_idx[j] < ii)) ? 1u : 0u;
-    }
-    if (rank < (uint32_t)a.k) {
-      a.values[(size_t)m * a.k + rank] = __uint_as_float(f_bits[i]);
-      a.indices[(size_t)m * a.k + rank] = (int64_t)ii;
-    }
-  }
+  for (int i = (int)n + (int)threadIdx.x; i < a.k; i += blockDim.x)
+    out[i] = make_uint2(0u, 0xFFFFFFFFu);
 }
 
 // ---------------------------------------------------------------------------
@@ -506,14 +625,21 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
 // ---------------------------------------------------------------------------
 namespace {
 
+// events: null, or two hipEvent_t that record the kernel's own start and end
 template <typename Arg>
-hipError_t launch1(void (*kern)(Arg), dim3 grid, dim3 block, size_t lds, void* stream, Arg arg) {
-  if (lds > 65536) {
+hipError_t launch1(void (*kern)(Arg), dim3 grid, dim3 block, size_t lds, void* stream, Arg arg,
+                   void* const* events = nullptr) {
+  if (lds > 32768) {  // with the kernel's static LDS the total may pass 64 KiB
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   void* args[] = {&arg};
+  if (events)
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, args, lds,
+                              static_cast<hipStream_t>(stream),
+                              static_cast<hipEvent_t>(events[0]),
+                              static_cast<hipEvent_t>(events[1]), 0);
   return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, args, lds,
                          static_cast<hipStream_t>(stream));
 }
@@ -590,7 +716,9 @@ void (*merge_kernel(int rm))(MergeArgs) {
 
 ChunkOut chunk_out(const Geometry& g, void* workspace) {
   ChunkOut o;
-  o.cand = static_cast<uint2*>(workspace);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  o.maxk = reinterpret_cast<uint32_t*>(ws);
+  o.cand = reinterpret_cast<uint2*>(ws + g.maxk_bytes);
   o.n_chunks = g.n_chunks;
   o.kc = g.kc;
   o.k = g.k;
@@ -601,7 +729,7 @@ ChunkOut chunk_out(const Geometry& g, void* workspace) {
 
 size_t binary_lds_bytes(int64_t M, int64_t H) {
   const int64_t G = H / kGroup;
-  return (size_t)(M * G * 8 * 16 + M * G * 4);
+  return (size_t)(512 + M * G * sizeof(TritGroup) + M * G * 4);
 }
 
 size_t dense_lds_bytes(int64_t M, int chunk_rows) { return (size_t)(M * chunk_rows * 4); }
@@ -636,7 +764,7 @@ int launch_pack(const void* w, int w_is_bf16, int64_t V, int64_t H, void* wq, fl
 
 int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* act_scale,
                          const void* wq, const float* wscale, const float* bias, int64_t H,
-                         void* workspace, void* stream) {
+                         void* workspace, void* stream, void* const* events) {
   BinaryArgs a;
   a.act_q = act_q;
   a.act_scale = act_scale;
@@ -652,11 +780,13 @@ int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* ac
   a.out = chunk_out(g, workspace);
   auto kern = binary_kernel((int)g.M, g.rpl);
   if (!kern) return (int)hipErrorInvalidValue;
-  return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), binary_lds_bytes(g.M, H), stream, a);
+  return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), binary_lds_bytes(g.M, H), stream, a,
+                      events);
 }
 
 int launch_dense_chunks(const Geometry& g, const void* hidden, const void* weight, int is_bf16,
-                        const float* bias, int64_t H, void* workspace, void* stream) {
+                        const float* bias, int64_t H, void* workspace, void* stream,
+                        void* const* events) {
   DenseArgs a;
   a.hidden = static_cast<const uint8_t*>(hidden);
   a.weight = static_cast<const uint8_t*>(weight);
@@ -668,11 +798,11 @@ int launch_dense_chunks(const Geometry& g, const void* hidden, const void* weigh
   auto kern = is_bf16 ? dense_kernel_b<true>((int)g.M, g.rpl) : dense_kernel_b<false>((int)g.M, g.rpl);
   if (!kern) return (int)hipErrorInvalidValue;
   return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), dense_lds_bytes(g.M, g.chunk_rows),
-                      stream, a);
+                      stream, a, events);
 }
 
 int launch_select_chunks(const Geometry& g, const float* logits, int64_t ld, void* workspace,
-                         void* stream) {
+                         void* stream, void* const* events) {
   SelectArgs a;
   a.logits = logits;
   a.M = g.M;
@@ -682,20 +812,25 @@ int launch_select_chunks(const Geometry& g, const float* logits, int64_t ld, voi
   a.out = chunk_out(g, workspace);
   auto kern = select_kernel(g.rpl);
   if (!kern) return (int)hipErrorInvalidValue;
-  return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), 0, stream, a);
+  return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), 0, stream, a, events);
 }
 
 int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* indices,
                   void* stream) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const uint32_t* maxk = reinterpret_cast<const uint32_t*>(ws);
+  ws += g.maxk_bytes;
   uint2* regions[2] = {reinterpret_cast<uint2*>(ws), reinterpret_cast<uint2*>(ws + g.region0_bytes)};
   for (int l = 0; l < g.n_levels; ++l) {
     const MergeLevel& L = g.level[l];
     MergeArgs a;
     a.in = regions[l & 1];
+    a.maxk = l == 0 ? maxk : nullptr;  // maxima describe the chunk candidates only
+    a.n_max = g.n_chunks;
     a.n_in = L.n_in;
     a.k = g.k;
     a.n_seg = L.n_seg;
+    a.threads = 64 * L.nw;
     a.seg = (int64_t)L.nw * 64 * L.rm;
     a.out = regions[(l + 1) & 1];
     a.values = values;
@@ -708,8 +843,5 @@ int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* in
   return 0;
 }
 
-int record_event(void* event, void* stream) {
-  return (int)hipEventRecord(static_cast<hipEvent_t>(event), static_cast<hipStream_t>(stream));
-}
 
 }  // namespace lmtopk

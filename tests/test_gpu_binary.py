@@ -217,7 +217,7 @@ def test_cfg2_invariants(cfg2):
     for _ in range(10):  # repeated calls are bitwise identical
         v, i = cfg2.run(50)
         assert torch.equal(i, i0) and torch.equal(v.view(torch.int32), v0.view(torch.int32))
-    for C in (256, 512, 2048, 4096):  # chunk size does not change a bit
+    for C in (64, 256, 512, 2048):  # chunk size does not change a bit
         v, i = cfg2.run(50, chunk_rows=C)
         assert torch.equal(i, i0) and torch.equal(v.view(torch.int32), v0.view(torch.int32))
     for m in range(2):  # a row alone equals the same row inside M=2

@@ -45,7 +45,7 @@ def test_tiny_brute_force_patterns():
 
 
 @pytest.mark.parametrize("k", [1, 7, 50, 64, 1024, 2048])
-@pytest.mark.parametrize("chunk_rows", [0, 64, 256, 1024, 2048, 4096])
+@pytest.mark.parametrize("chunk_rows", [0, 64, 192, 256, 1024, 2048])
 def test_random_rows_all_chunk_sizes(k, chunk_rows):
     x = synthetic.random_logits(3, 50000, seed=11)
     v, i = run_select(x, k, chunk_rows)
@@ -124,3 +124,57 @@ def test_repeat_bitwise_identical():
         v, i = lt.topk_logits(t, 50)
         assert torch.equal(i, i0) and torch.equal(v.view(torch.int32), v0.view(torch.int32))
     assert_select_exact(x, v0.cpu().numpy(), i0.cpu().numpy(), 50)
+
+
+@pytest.mark.parametrize("copies", [1, 2, 3, 50])
+def test_equal_chunk_maxima_bound_and_fallback(copies):
+    # Every 1024-row chunk of a 248,320-entry row peaks at the same value, in
+    # `copies` places: the k-th largest chunk maximum then equals the k-th
+    # largest logit, and 243 * copies candidates tie with it (fewer or more
+    # than the merge's survivor buffer holds), so the answer is the k lowest
+    # indices holding the peak.
+    V, C, k = 248320, 1024, 50
+    x = synthetic.random_logits(2, V, seed=copies)
+    x = np.minimum(x, np.float32(3.0))
+    for c in range(0, V, C):
+        for j in range(copies):
+            x[:, c + 10 * j + 5] = np.float32(4.0)  # inside the 512-row last chunk too
+    x[1] = -x[1]  # row 1: peaks become minima, its own random maxima decide
+    v, i = run_select(x, k, C)
+    assert_select_exact(x, v, i, k)
+    peaks = np.flatnonzero(x[0] == np.float32(4.0))
+    assert np.array_equal(i[0], peaks[:k])
+
+
+def _hip_runtime():
+    import ctypes
+    with open("/proc/self/maps") as f:
+        path = next(line.split()[-1] for line in f if "libamdhip64" in line)
+    hip = ctypes.CDLL(path)
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def test_score_events_time_the_scoring_kernel():
+    # the options' event pair records the scoring kernel's own start and end;
+    # results are unchanged
+    import ctypes
+    torch.zeros(1, device="cuda")
+    hip = _hip_runtime()
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    x = synthetic.random_logits(2, 248320, seed=4)
+    t = dev(x)
+    v0, i0 = lt.topk_logits(t, 50)
+    v1, i1 = lt.topk_logits(t, 50, score_events=(ev[0], ev[1]))
+    torch.cuda.synchronize()
+    ms = ctypes.c_float()
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+    assert 0.0 < ms.value < 100.0
+    assert torch.equal(i0, i1) and torch.equal(v0.view(torch.int32), v1.view(torch.int32))
+    for e in ev:
+        hip.hipEventDestroy(e)
