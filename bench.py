@@ -169,7 +169,7 @@ def summarize_pmc(fetch_dir, write_dir, name, command):
         vals = [v for k in ks for v in per[k]]
         return statistics.median(vals), len(vals)
 
-    copy_sub = "elementwise"
+    copy_sub = "MulFunctor"  # the plain copy of plain_copy_gbps
     f_copy, _ = pick(fetch, copy_sub)
     w_copy, _ = pick(write, copy_sub)
     f_scale = COPY_BYTES / (f_copy * 1024.0)
@@ -372,14 +372,16 @@ def main():
     warm_ms, _, _ = time_calls(hip, stream, lambda i, ev: call(i, ev, 1), args.steps, False)
     warm_us = warm_ms / args.steps * 1e3
     log(f"score kernel {score_us:.2f} us, merge {merge_us:.2f} us; single-copy (cache) {warm_us:.2f} us/step")
+    # per-call spread: scoring kernel start to the end of the call's merge
+    call_us = sorted((a + b) * 1e3 for a, b in zip(score_ms, merge_ms))
+    pct = lambda q: round(call_us[min(len(call_us) - 1, int(q * len(call_us)))], 3)
+    graph_us = graph_replay_us(args, call, hip, stream, vals, idx)
+    log(f"per call p10/p50/p90 {pct(0.1)}/{pct(0.5)}/{pct(0.9)} us; hipGraph replay {graph_us} us/step")
+    stream_gbps = plain_copy_gbps(hip, stream, dev)
+    log(f"plain 1 GiB copy: {stream_gbps:.0f} GB/s read + written")
 
-    # plain copy of known size (counter calibration for --summarize-pmc)
-    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        torch.mul(src, 1.0, out=dst)
-    torch.cuda.synchronize()
-    del src, dst
+    # (plain_copy_gbps above also serves as the counter calibration of
+    # --summarize-pmc: a copy of known size)
 
     head_bytes = sum(lt.packed_bytes(V, H))
     alg_bytes = algorithmic_score_bytes(M, V, H, k, args.bias, args.chunk_rows, lt)
@@ -410,6 +412,9 @@ def main():
                      "traffic": traffic, "kernel": SCORE_KERNEL, "algorithmic_bytes": alg_bytes,
                      "avg_kernel_us": round(score_us, 3)},
         "kernels_us": {"score_select": round(score_us, 3), "merge_and_gap": round(merge_us, 3)},
+        "per_call_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
+        "graph_replay_us_per_step": graph_us,
+        "plain_copy_gbps_1gib": round(stream_gbps, 1),
         "cache_served_single_copy": {"us_per_token": round(warm_us / M, 3),
                                      "gbps": round(head_bytes / (warm_us * 1e-6) / 1e9, 1)},
     }
@@ -420,6 +425,49 @@ def main():
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(args, W, act_q, act_scale, bias)
     print(json.dumps(result), flush=True)
+
+
+def graph_replay_us(args, call, hip, stream, vals, idx):
+    """The same rotated calls captured once in a hipGraph and replayed: the
+    difference to the eager loop is host launch cost that the spin in front
+    of the eager loop does not already hide.  Checks that a replay leaves
+    the eager result."""
+    import torch
+    call(0, None)
+    torch.cuda.synchronize()
+    ref_v, ref_i = vals.clone(), idx.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(args.copies):
+                call(i, None)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // args.copies)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    if not (torch.equal(idx, ref_i) and torch.equal(vals.view(torch.int32), ref_v.view(torch.int32))):
+        raise RuntimeError("graph replay result differs from the eager call")
+    t, _, _ = time_calls(hip, torch.cuda.current_stream().cuda_stream, lambda i, ev: g.replay(), reps,
+                         False)
+    del g
+    return round(t / (reps * args.copies) * 1e3, 3)
+
+
+def plain_copy_gbps(hip, stream, dev):
+    """Achievable HBM rate on this machine for plain streaming: torch's elementwise
+    copy of 1 GiB (bytes read + bytes written per second)."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    t, _, _ = time_calls(hip, stream, lambda i, ev: torch.mul(src, 1.0, out=dst), 10, False)
+    del src, dst
+    return 2 * COPY_BYTES / (t / 10 * 1e-3) / 1e9
 
 
 def materialized_comparison(args, lt, hip, stream, dev):

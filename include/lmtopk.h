@@ -134,9 +134,9 @@ lmtopk_status lmtopk_packed_bytes(int64_t V, int64_t H, int32_t group_size,
 
 /* Host-only: workspace bytes needed by lmtopk_binary, lmtopk_dense and
    lmtopk_select for these sizes and options.  The same workspace serves all
-   three.  It holds, per row, the largest logit of every chunk and the chunk
-   candidates (8 bytes each), plus one intermediate merge level when a row
-   has more than 16384 candidates.
+   three.  It holds, per row and chunk, the chunk's four best candidates and
+   all its candidates (8 bytes each), plus one intermediate merge level when
+   a row has more than 16384 candidates.
    Errors: NULL, SHAPE, K, OPTIONS. */
 lmtopk_status lmtopk_workspace_bytes(int64_t M, int64_t V, int32_t k,
                                      const lmtopk_options* opt, size_t* bytes);

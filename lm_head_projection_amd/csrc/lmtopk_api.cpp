@@ -60,7 +60,7 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, Geome
   g->n_chunks = (int)((V + C - 1) / C);
   g->kc = k < C ? k : C;
   const int64_t n0 = (int64_t)g->n_chunks * g->kc;
-  g->maxk_bytes = round_up((size_t)(M * g->n_chunks * 4), 256);
+  g->heads_bytes = round_up((size_t)(M * g->n_chunks * 4 * 8), 256);
   g->region0_bytes = round_up((size_t)(M * n0 * 8), 256);
 
   // merge plan: a level either fits one workgroup (final) or splits the
@@ -94,7 +94,7 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, Geome
     ++lv;
   }
   g->n_levels = lv;
-  g->workspace_bytes = g->maxk_bytes + g->region0_bytes + g->region1_bytes;
+  g->workspace_bytes = g->heads_bytes + g->region0_bytes + g->region1_bytes;
   return LMTOPK_OK;
 }
 

@@ -302,6 +302,45 @@ __device__ uint32_t block_compact(const uint32_t (&key)[R], uint32_t valid, cons
   return selected;
 }
 
+// Chunk heads: besides its candidates in index order, every chunk writes its
+// kHeads best candidates in output order (value desc, index asc), padded with
+// index -1.  The merge reads only these heads unless a chunk may hold more
+// winners than its heads.
+constexpr int kHeads = 4;
+
+// The candidates of one chunk row as the compaction placed them (index order).
+struct alignas(16) HeadStage {
+  uint32_t key[kMaxK];
+  uint32_t bits[kMaxK];
+  int32_t idx[kMaxK];
+};
+
+// Wave 0 only: the kHeads best of st[0, n) in output order -> heads[0, kHeads).
+// Round s takes the largest remaining key, the lowest staging position among
+// equal keys (staging order is index order), and retires it.
+__device__ void write_heads(HeadStage& st, uint32_t n, uint2* heads) {
+  const uint32_t lane = (uint32_t)lane_id();
+#pragma unroll 1
+  for (int h = 0; h < kHeads; ++h) {
+    uint32_t best = 0u, best_e = 0xFFFFFFFFu;
+    for (uint32_t e = lane; e < n; e += 64) {
+      const uint32_t kk = st.key[e];
+      if (kk > best) {  // strict: the lower position wins a tie
+        best = kk;
+        best_e = e;
+      }
+    }
+    const uint32_t wm = wave_max_u32(best);
+    uint2 out = make_uint2(0u, 0xFFFFFFFFu);
+    if (wm != 0u) {
+      const uint32_t e = wave_min_u32(best == wm ? best_e : 0xFFFFFFFFu);
+      out = make_uint2(st.bits[e], (uint32_t)st.idx[e]);
+      if (lane == (e & 63u)) st.key[e] = 0u;  // retired (0 is below every real key)
+    }
+    if (lane == 0) heads[h] = out;
+  }
+}
+
 // LDS of the final merge: up to kMaxK entries to sort (4 slack entries so the
 // rank loop can read whole uint4 words), their ranks, and two scalars.
 struct alignas(16) FinalSmem {
@@ -309,8 +348,10 @@ struct alignas(16) FinalSmem {
   uint32_t bits[kMaxK + 4];
   int32_t idx[kMaxK + 4];
   uint32_t rank[kMaxK + 4];
-  uint32_t count;  // survivors placed so far
-  uint32_t bound;  // survivor threshold (a key)
+  uint32_t count;   // survivors placed so far
+  uint32_t bound;   // survivor threshold (a key)
+  uint32_t n_over;  // chunks whose heads may not hold all their survivors
+  int32_t over[256];
 };
 
 // Entries [0, n) of fs are filled, [n, 4 * ceil(n / 4)) hold padding that is
@@ -404,53 +445,70 @@ __device__ __forceinline__ uint32_t wave_bound(uint32_t (&m)[4], int n_max, uint
   return prefix;
 }
 
-// Final merge of one row.  `in` holds n_in candidates (fp32 value bits, int32
-// index) in ascending index order, index -1 = padding; RM slots per thread
-// cover them (n_in <= blockDim.x * RM).  `maxk` (optional) holds the largest
-// key of each of the n_max chunks the candidates came from.  Writes the exact
-// top-k sorted by (value desc, index asc).
+// Puts this lane's entry into the survivor list if `take`: one LDS atomic per
+// wave reserves the wave's slots; entries past kSurvivorsMax are counted but
+// not stored (the caller then falls back).
+constexpr uint32_t kSurvivorsMax = 512;
+
+__device__ __forceinline__ void place_survivor(FinalSmem& fs, bool take, uint32_t key,
+                                               uint32_t bits, int32_t ix) {
+  const uint64_t b = ballot(take);
+  if (b == 0u) return;
+  uint32_t base = 0;
+  if (lane_id() == 0) base = atomicAdd(&fs.count, (uint32_t)__popcll(b));
+  base = readlane_u32(base, 0);
+  const uint32_t p = base + lanes_below(b);
+  if (take && p < kSurvivorsMax) {
+    fs.key[p] = key;
+    fs.bits[p] = bits;
+    fs.idx[p] = ix;
+  }
+}
+
+// Final merge of one row.  `in` holds the n_in candidates of the n_max chunks
+// (kc per chunk, fp32 value bits and int32 index, index -1 = padding) in
+// ascending index order; RM slots per thread cover them (n_in <=
+// blockDim.x * RM).  `heads` (optional) holds each chunk's kHeads best
+// candidates in output order.  Writes the exact top-k sorted by (value desc,
+// index asc).
 //
 // Bounded path: a threshold T with at least k chunk maxima >= T is at most
 // the row's k-th largest value (those maxima are k distinct logits), so only
-// candidates with key >= T can be in the result.  Wave 0 finds T while the
-// candidate loads of every wave are still in flight; the survivors (typically
-// a few dozen) go to LDS in any order and are ranked there.  When there are
-// too many chunks or survivors, the radix select of all candidates runs
-// instead.
-constexpr uint32_t kSurvivorsMax = 512;
-
+// candidates with key >= T can be in the result.  Wave 0 finds T from the
+// heads' first entries.  A chunk whose last head is below T has all its
+// survivors among its heads; the few other chunks (typically none) are read
+// in full.  The survivors (typically a few dozen) go to LDS in any order and
+// are ranked there.  With too many chunks or survivors, the radix select of
+// all candidates runs instead.
 template <int RM>
-__device__ void merge_final(const uint2* in, int64_t n_in, const uint32_t* maxk, int n_max,
+__device__ void merge_final(const uint2* in, int64_t n_in, const uint2* heads, int n_max, int kc,
                             uint32_t k, float* values, int64_t* indices, int nthreads,
                             SelectSmem& sm, FinalSmem& fs) {
   // nthreads == blockDim.x, passed in so that no load of it queues behind
-  // the candidate loads
+  // the data loads
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
-  const bool bounded = maxk != nullptr && n_max >= (int)k && n_max <= 256;
+  const int n_heads = n_max * kHeads;
 
-  // Every load is unconditional (addresses clamped into the arrays, the
-  // extra entries marked invalid) so that all of them are in flight at once.
-  uint32_t m[4] = {0u, 0u, 0u, 0u};
-  if (bounded && wave == 0) {  // issued first: the bound only waits for these
-#pragma unroll
-    for (int r = 0; r < 4; ++r) m[r] = maxk[min(r * 64 + lane, n_max - 1)];
-  }
-  uint32_t key[RM], vb[RM];
-  int32_t idx[RM];
-  uint32_t inside = 0u;  // slots that lie in [0, n_in); known before the loads land
-#pragma unroll
-  for (int r = 0; r < RM; ++r) {
-    const int64_t pos = (int64_t)(wave * RM + r) * 64 + lane;
-    const uint2 e = in[pos < n_in ? pos : n_in - 1];
-    vb[r] = e.x;
-    idx[r] = (int32_t)e.y;
-    inside |= (pos < n_in ? 1u : 0u) << r;
-  }
   for (int i = tid; i < kMaxK + 4; i += nthreads) fs.rank[i] = 0u;
 
-  if (bounded) {
+  if (heads != nullptr && n_max >= (int)k && n_max <= 256 && n_heads <= nthreads) {
+    // Loads are unconditional (indices clamped into the arrays) so that all
+    // of them are in flight at once; the maxima go first, the bound waits
+    // only for them.
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+    if (wave == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = min(r * 64 + lane, n_max - 1);
+        m[r] = float_key(__uint_as_float(heads[(size_t)c * kHeads].x));
+      }
+    }
+    const int e = min(tid, n_heads - 1);
+    const int c = e / kHeads;
+    const uint2 he = heads[e];
+    const uint2 hl = heads[(size_t)c * kHeads + (kHeads - 1)];
     for (int i = tid; i < (int)kSurvivorsMax + 4; i += nthreads) {
       fs.key[i] = 0u;  // padding: below every real key
       fs.idx[i] = 0x7FFFFFFF;
@@ -460,44 +518,35 @@ __device__ void merge_final(const uint2* in, int64_t n_in, const uint32_t* maxk,
       if (lane == 0) {
         fs.bound = t;
         fs.count = 0u;
+        fs.n_over = 0u;
       }
     }
     lds_barrier();
-  }
-  // keys and validity only now, so that wave 0 found the bound without
-  // waiting for its candidate loads
-  uint32_t valid = 0u;
-#pragma unroll
-  for (int r = 0; r < RM; ++r) {
-    key[r] = float_key(__uint_as_float(vb[r]));
-    valid |= (((inside >> r) & 1u) && idx[r] >= 0 ? 1u : 0u) << r;
-  }
-  if (bounded) {
     const uint32_t t = fs.bound;
-    // survivors of this wave go to a block of slots reserved with one atomic
-    uint64_t sv[RM];
-    uint32_t nsv = 0;
-#pragma unroll
-    for (int r = 0; r < RM; ++r) {
-      sv[r] = ballot(((valid >> r) & 1u) && key[r] >= t);
-      nsv += (uint32_t)__popcll(sv[r]);
-    }
-    if (nsv) {
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&fs.count, nsv);
-      base = readlane_u32(base, 0);
-#pragma unroll
-      for (int r = 0; r < RM; ++r) {
-        const uint32_t p = base + lanes_below(sv[r]);
-        if (((sv[r] >> lane) & 1u) && p < kSurvivorsMax) {
-          fs.key[p] = key[r];
-          fs.bits[p] = vb[r];
-          fs.idx[p] = idx[r];
-        }
-        base += (uint32_t)__popcll(sv[r]);
-      }
-    }
+    const bool mine = tid < n_heads && (int32_t)he.y >= 0;
+    const uint32_t key = float_key(__uint_as_float(he.x));
+    // a chunk with more candidates than heads may hold survivors beyond them
+    const bool over = kc > kHeads && (int32_t)hl.y >= 0 && float_key(__uint_as_float(hl.x)) >= t;
+    place_survivor(fs, mine && !over && key >= t, key, he.x, (int32_t)he.y);
+    if (tid < n_heads && over && e == c * kHeads) fs.over[atomicAdd(&fs.n_over, 1u)] = c;
     lds_barrier();
+    const uint32_t n_over = fs.n_over;
+    if (n_over) {  // rare: read those chunks' candidate lists in full
+      const int64_t total = (int64_t)n_over * kc;
+      for (int64_t base = 0; base < total; base += nthreads) {
+        const int64_t j = base + tid;
+        bool take = false;
+        uint2 x = make_uint2(0u, 0xFFFFFFFFu);
+        uint32_t kx = 0u;
+        if (j < total) {
+          x = in[(int64_t)fs.over[j / kc] * kc + j % kc];
+          kx = float_key(__uint_as_float(x.x));
+          take = (int32_t)x.y >= 0 && kx >= t;
+        }
+        place_survivor(fs, take, kx, x.x, (int32_t)x.y);
+      }
+      lds_barrier();
+    }
     const uint32_t n = fs.count;
     if (n <= kSurvivorsMax) {
       rank_and_write(fs, n, k, values, indices);
@@ -505,6 +554,20 @@ __device__ void merge_final(const uint2* in, int64_t n_in, const uint32_t* maxk,
     }
   }
 
+  // Full path: radix select over every candidate (slot order = index order),
+  // ordered compaction, rank.
+  uint32_t key[RM], vb[RM];
+  int32_t idx[RM];
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int r = 0; r < RM; ++r) {
+    const int64_t pos = (int64_t)(wave * RM + r) * 64 + lane;
+    const uint2 x = in[pos < n_in ? pos : n_in - 1];
+    vb[r] = x.x;
+    idx[r] = (int32_t)x.y;
+    key[r] = float_key(__uint_as_float(x.x));
+    valid |= (pos < n_in && idx[r] >= 0 ? 1u : 0u) << r;
+  }
   const SelectRange s = block_select<RM>(key, valid, k, sm);
   const uint32_t n = block_compact<RM>(key, valid, s, vb, idx, sm,
                                        [&](uint32_t pos, uint32_t bits, int32_t ix) {
@@ -512,7 +575,7 @@ __device__ void merge_final(const uint2* in, int64_t n_in, const uint32_t* maxk,
                                          fs.bits[pos] = bits;
                                          fs.idx[pos] = ix;
                                        });
-  for (uint32_t i = n + tid; i < ((n + 3u) & ~3u); i += blockDim.x) {
+  for (uint32_t i = n + tid; i < ((n + 3u) & ~3u); i += nthreads) {
     fs.key[i] = 0u;
     fs.idx[i] = 0x7FFFFFFF;
   }

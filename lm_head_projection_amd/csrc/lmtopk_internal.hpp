@@ -30,7 +30,7 @@ struct Geometry {
   int64_t n_tiles; // 64-row tiles covering V
   int n_levels;    // merge kernel launches
   MergeLevel level[kMaxMergeLevels];
-  size_t maxk_bytes;     // largest key of each chunk [M][n_chunks] x 4 B
+  size_t heads_bytes;    // best candidates of each chunk [M][n_chunks][4] x 8 B
   size_t region0_bytes;  // chunk candidates [M][n_chunks * kc] x 8 B
   size_t region1_bytes;  // first intermediate merge output, or 0
   size_t workspace_bytes;

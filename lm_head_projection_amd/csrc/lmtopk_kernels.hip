@@ -100,19 +100,20 @@ __global__ __launch_bounds__(256) void k_pack(const void* __restrict__ w, int64_
 // shared pieces of the chunk kernels
 // ---------------------------------------------------------------------------
 struct ChunkOut {
-  uint2* cand;      // [M][n_chunks][kc]
-  uint32_t* maxk;   // [M][n_chunks] largest key of each chunk
+  uint2* cand;   // [M][n_chunks][kc]
+  uint2* heads;  // [M][n_chunks][kHeads]
   int n_chunks;
   int kc;
   int k;
 };
 
 // Selects the chunk's top-k of row m from RPL slots per lane and writes them
-// (ascending index) followed by padding up to kc entries.
+// (ascending index) followed by padding up to kc entries, then the chunk's
+// heads.  `last` = no further row follows in this workgroup.
 template <int RPL>
 __device__ __forceinline__ void chunk_select_write(const float (&val)[RPL], const int32_t (&idx)[RPL],
                                                    uint32_t valid, int m, const ChunkOut& o,
-                                                   SelectSmem& sm) {
+                                                   SelectSmem& sm, HeadStage& st, bool last) {
   uint32_t key[RPL], vb[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
@@ -120,14 +121,20 @@ __device__ __forceinline__ void chunk_select_write(const float (&val)[RPL], cons
     key[r] = float_key(val[r]);
   }
   const SelectRange s = block_select<RPL>(key, valid, (uint32_t)o.k, sm);
-  if (threadIdx.x == 0) o.maxk[(size_t)m * o.n_chunks + blockIdx.x] = s.kmax;
-  uint2* out = o.cand + ((size_t)m * o.n_chunks + blockIdx.x) * o.kc;
+  const size_t row_chunk = (size_t)m * o.n_chunks + blockIdx.x;
+  uint2* out = o.cand + row_chunk * o.kc;
   const uint32_t n = block_compact<RPL>(key, valid, s, vb, idx, sm,
                                         [&](uint32_t pos, uint32_t bits, int32_t ix) {
                                           out[pos] = make_uint2(bits, (uint32_t)ix);
+                                          st.key[pos] = float_key(__uint_as_float(bits));
+                                          st.bits[pos] = bits;
+                                          st.idx[pos] = ix;
                                         });
   for (int i = (int)n + (int)threadIdx.x; i < o.kc; i += blockDim.x)
     out[i] = make_uint2(0u, 0xFFFFFFFFu);
+  lds_barrier();
+  if ((threadIdx.x >> 6) == 0) write_heads(st, n, o.heads + row_chunk * kHeads);
+  if (!last) lds_barrier();  // the staging is refilled by the next row
 }
 
 // ---------------------------------------------------------------------------
@@ -208,6 +215,7 @@ template <int M, int R>
 __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs a) {
   extern __shared__ __align__(16) uint8_t dyn_lds[];
   __shared__ SelectSmem ssm;
+  __shared__ HeadStage hst;
   const int G = a.G;
   uint16_t* table = reinterpret_cast<uint16_t*>(dyn_lds);             // [256] trit codes
   TritGroup* tgs = reinterpret_cast<TritGroup*>(dyn_lds + 512);       // [M][G]
@@ -295,10 +303,32 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     load_acts(b0, y0, y1);
     build_masks(b0, y0, y1);
   }
-  // 3. the first batch's activation bytes
+  // 3. the first batch's activation bytes, this lane's bias and the row
+  //    scales (loaded now: after the main loop a load would cost a full
+  //    memory round trip in the tail)
   int8_t x0[kBatch], x1[kBatch];
   load_acts(wave, x0, x1);
-  __builtin_amdgcn_sched_barrier(0);  // the activation loads stay ahead of the weight loads
+  float bias_v[R];
+  {
+    // unconditional loads from valid addresses; the values are used only
+    // for real rows of a real bias
+    const float* bp = a.bias != nullptr ? a.bias : a.act_scale;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int64_t v = (tile0 + r) * 64 + lane;
+      v = a.bias != nullptr ? (v < a.V ? v : a.V - 1) : 0;
+      bias_v[r] = bp[v];
+    }
+  }
+  float act_s[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) act_s[m] = a.act_scale[m];
+  __builtin_amdgcn_sched_barrier(0);
+  // every wave's activation requests go out before any wave's weight
+  // requests: the CU serves its requests in order, so otherwise the last
+  // waves would wait for most of the weight prefetch before they could build
+  // their masks
+  lds_barrier();
 
   // 4. first two quads of weights (group and quad indices clamped into the head)
   //    (issued in the same order as the main loop's refills: all of quad 0,
@@ -399,22 +429,21 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
 
   int32_t idx[R];
   uint32_t valid = 0u;
-  float bias_v[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t v = (tile0 + r) * 64 + lane;
     idx[r] = (int32_t)v;
     const bool vv = (tile0 + r) < a.n_tiles && v < a.V;
     valid |= (vv ? 1u : 0u) << r;
-    bias_v[r] = (a.bias != nullptr && vv) ? a.bias[v] : 0.f;
+    if (a.bias == nullptr || !vv) bias_v[r] = 0.f;
   }
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const float s = a.act_scale[m];
+    const float s = act_s[m];
     float val[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) val[r] = fmaf(acc[r][m], s, bias_v[r]);
-    chunk_select_write<R>(val, idx, valid, m, a.out, ssm);
+    chunk_select_write<R>(val, idx, valid, m, a.out, ssm, hst, m == M - 1);
   }
 }
 
@@ -458,6 +487,7 @@ template <int M, bool BF16, int RPL>
 __global__ __launch_bounds__(1024) void k_dense_chunk(DenseArgs a) {
   extern __shared__ __align__(16) uint8_t dyn_lds[];
   __shared__ SelectSmem ssm;
+  __shared__ HeadStage hst;
   float* scores = reinterpret_cast<float*>(dyn_lds);  // [M][C]
   const int C = a.chunk_rows;
   const int tid = threadIdx.x;
@@ -521,7 +551,7 @@ __global__ __launch_bounds__(1024) void k_dense_chunk(DenseArgs a) {
     float val[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r) val[r] = ((valid >> r) & 1u) ? scores[m * C + lr[r]] : 0.f;
-    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm);
+    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm, hst, m == M - 1);
   }
 }
 
@@ -538,6 +568,7 @@ struct SelectArgs {
 template <int RPL>
 __global__ __launch_bounds__(1024) void k_select_chunk(SelectArgs a) {
   __shared__ SelectSmem ssm;
+  __shared__ HeadStage hst;
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
   const int64_t base = (int64_t)blockIdx.x * a.chunk_rows;
@@ -554,7 +585,7 @@ __global__ __launch_bounds__(1024) void k_select_chunk(SelectArgs a) {
     float val[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r) val[r] = ((valid >> r) & 1u) ? row[idx[r]] : 0.f;
-    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm);
+    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm, hst, m == (int)a.M - 1);
   }
 }
 
@@ -563,8 +594,9 @@ __global__ __launch_bounds__(1024) void k_select_chunk(SelectArgs a) {
 // ---------------------------------------------------------------------------
 struct MergeArgs {
   const uint2* in;  // [M][n_in] candidates, ascending index within each row
-  const uint32_t* maxk;  // [M][n_max] chunk maxima for the bound, or null
-  int n_max;
+  const uint2* heads;  // [M][n_max][kHeads] chunk heads, or null
+  int n_max;           // chunks
+  int kc;              // candidates per chunk
   int64_t n_in;
   int k;
   int threads;      // blockDim.x
@@ -588,8 +620,8 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
   const uint2* in = a.in + (size_t)m * a.n_in;
   if (a.n_seg == 1) {
     __shared__ FinalSmem fs;
-    merge_final<RM>(in, a.n_in, a.maxk ? a.maxk + (size_t)m * a.n_max : nullptr, a.n_max,
-                    (uint32_t)a.k, a.values + (size_t)m * a.k, a.indices + (size_t)m * a.k,
+    merge_final<RM>(in, a.n_in, a.heads ? a.heads + (size_t)m * a.n_max * kHeads : nullptr,
+                    a.n_max, a.kc, (uint32_t)a.k, a.values + (size_t)m * a.k, a.indices + (size_t)m * a.k,
                     a.threads, ssm, fs);
     return;
   }
@@ -717,8 +749,8 @@ void (*merge_kernel(int rm))(MergeArgs) {
 ChunkOut chunk_out(const Geometry& g, void* workspace) {
   ChunkOut o;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  o.maxk = reinterpret_cast<uint32_t*>(ws);
-  o.cand = reinterpret_cast<uint2*>(ws + g.maxk_bytes);
+  o.heads = reinterpret_cast<uint2*>(ws);
+  o.cand = reinterpret_cast<uint2*>(ws + g.heads_bytes);
   o.n_chunks = g.n_chunks;
   o.kc = g.kc;
   o.k = g.k;
@@ -818,15 +850,16 @@ int launch_select_chunks(const Geometry& g, const float* logits, int64_t ld, voi
 int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* indices,
                   void* stream) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const uint32_t* maxk = reinterpret_cast<const uint32_t*>(ws);
-  ws += g.maxk_bytes;
+  const uint2* heads = reinterpret_cast<const uint2*>(ws);
+  ws += g.heads_bytes;
   uint2* regions[2] = {reinterpret_cast<uint2*>(ws), reinterpret_cast<uint2*>(ws + g.region0_bytes)};
   for (int l = 0; l < g.n_levels; ++l) {
     const MergeLevel& L = g.level[l];
     MergeArgs a;
     a.in = regions[l & 1];
-    a.maxk = l == 0 ? maxk : nullptr;  // maxima describe the chunk candidates only
+    a.heads = l == 0 ? heads : nullptr;  // heads describe the chunk candidates only
     a.n_max = g.n_chunks;
+    a.kc = g.kc;
     a.n_in = L.n_in;
     a.k = g.k;
     a.n_seg = L.n_seg;

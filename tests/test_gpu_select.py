@@ -178,3 +178,25 @@ def test_score_events_time_the_scoring_kernel():
     assert torch.equal(i0, i1) and torch.equal(v0.view(torch.int32), v1.view(torch.int32))
     for e in ev:
         hip.hipEventDestroy(e)
+
+
+@pytest.mark.parametrize("layout", ["one_chunk", "last_chunk", "five_per_chunk", "k_above_heads"])
+def test_merge_reads_whole_chunks_when_heads_may_not_suffice(layout):
+    # 243 chunks of 1024 rows: the merge bounds the survivors by the chunk
+    # maxima and reads only each chunk's four best candidates, except for
+    # chunks whose fourth best passes the bound; these layouts force that.
+    V, C = 248320, 1024
+    k = 50
+    x = synthetic.random_logits(1, V, seed=21)
+    if layout == "one_chunk":
+        x[0, 7 * C + 3: 7 * C + 3 + 50 * 19: 19] += np.float32(100.0)
+    elif layout == "last_chunk":
+        last = (V - 1) // C * C
+        x[0, last: last + 50] += np.float32(100.0)
+    elif layout == "five_per_chunk":
+        for c in range(0, 30 * C, 3 * C):  # 10 chunks, 5 winners each
+            x[0, c + 100: c + 105] += np.float32(50.0)
+    else:
+        k = 200  # k-th best far below the chunk maxima: many chunks pass
+    v, i = run_select(x, k, C)
+    assert_select_exact(x, v, i, k)
