@@ -36,7 +36,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "_lib", "liblmtopk.so")
+# LMTOPK_LIBRARY names another build of the same library to load instead
+# (for comparing builds); by default the in-tree build is loaded.
+_LIB_PATH = os.environ.get("LMTOPK_LIBRARY") or os.path.join(_HERE, "_lib", "liblmtopk.so")
 
 GROUP_SIZE = 128
 MAX_ROWS = 8

@@ -201,7 +201,7 @@ lmtopk_status lmtopk_binary(const int8_t* act_q, const float* act_scale, const v
     return LMTOPK_ERR_ALIGN;
   size_t lds_max = 0;
   if (lmtopk::max_lds_per_block(&lds_max)) return LMTOPK_ERR_HIP;
-  if (lmtopk::binary_lds_bytes(M, H) + 32768 > lds_max) return LMTOPK_ERR_SHAPE;
+  if (lmtopk::binary_lds_bytes(M, H) + lmtopk::kChunkStaticLds > lds_max) return LMTOPK_ERR_SHAPE;
   const int e =
       lmtopk::launch_binary_chunks(g, act_q, act_scale, wq, wscale, bias, H, workspace, stream,
                                    score_events(opt));
@@ -225,7 +225,8 @@ lmtopk_status lmtopk_dense(const void* hidden, const void* weight, lmtopk_dtype 
     return LMTOPK_ERR_ALIGN;
   size_t lds_max = 0;
   if (lmtopk::max_lds_per_block(&lds_max)) return LMTOPK_ERR_HIP;
-  if (lmtopk::dense_lds_bytes(M, g.chunk_rows) + 32768 > lds_max) return LMTOPK_ERR_SHAPE;
+  if (lmtopk::dense_lds_bytes(M, g.chunk_rows) + lmtopk::kChunkStaticLds > lds_max)
+    return LMTOPK_ERR_SHAPE;
   const int e = lmtopk::launch_dense_chunks(g, hidden, weight, dtype == LMTOPK_BF16, bias, H,
                                             workspace, stream, score_events(opt));
   return finish(g, e, workspace, values, indices, stream);

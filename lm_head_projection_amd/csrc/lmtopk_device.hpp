@@ -313,31 +313,40 @@ struct alignas(16) HeadStage {
   uint32_t key[kMaxK];
   uint32_t bits[kMaxK];
   int32_t idx[kMaxK];
+  uint32_t rank[kMaxK];  // zero between uses
 };
 
-// Wave 0 only: the kHeads best of st[0, n) in output order -> heads[0, kHeads).
-// Round s takes the largest remaining key, the lowest staging position among
-// equal keys (staging order is index order), and retires it.
+// The kHeads best of st[0, n) in output order -> heads[0, kHeads), padded
+// with index -1.  Every entry's position in the output order is the number of
+// entries ahead of it (greater key, or equal key and earlier staging position,
+// which is the lower index); the count for entry i is split over
+// blockDim / n threads and summed with LDS atomics; entries with a position
+// below kHeads write themselves.  Called by the whole workgroup; st.rank must
+// be zero on entry and is zero again on return.
 __device__ void write_heads(HeadStage& st, uint32_t n, uint2* heads) {
-  const uint32_t lane = (uint32_t)lane_id();
-#pragma unroll 1
-  for (int h = 0; h < kHeads; ++h) {
-    uint32_t best = 0u, best_e = 0xFFFFFFFFu;
-    for (uint32_t e = lane; e < n; e += 64) {
-      const uint32_t kk = st.key[e];
-      if (kk > best) {  // strict: the lower position wins a tie
-        best = kk;
-        best_e = e;
-      }
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  if (tid >= n && tid < (uint32_t)kHeads) heads[tid] = make_uint2(0u, 0xFFFFFFFFu);
+  if (n == 0) return;
+  uint32_t segs = nt / n;
+  segs = segs < 1u ? 1u : (segs > n ? n : segs);
+  const uint32_t per = (n + segs - 1u) / segs;
+  for (uint32_t t = tid; t < n * segs; t += nt) {
+    const uint32_t i = t % n;
+    const uint32_t j0 = (t / n) * per;
+    const uint32_t j1 = min(n, j0 + per);
+    const uint32_t ki = st.key[i];
+    uint32_t ahead = 0;
+    for (uint32_t j = j0; j < j1; ++j) {
+      const uint32_t kj = st.key[j];
+      ahead += (kj > ki || (kj == ki && j < i)) ? 1u : 0u;
     }
-    const uint32_t wm = wave_max_u32(best);
-    uint2 out = make_uint2(0u, 0xFFFFFFFFu);
-    if (wm != 0u) {
-      const uint32_t e = wave_min_u32(best == wm ? best_e : 0xFFFFFFFFu);
-      out = make_uint2(st.bits[e], (uint32_t)st.idx[e]);
-      if (lane == (e & 63u)) st.key[e] = 0u;  // retired (0 is below every real key)
-    }
-    if (lane == 0) heads[h] = out;
+    if (ahead) atomicAdd(&st.rank[i], ahead);
+  }
+  lds_barrier();
+  for (uint32_t i = tid; i < n; i += nt) {
+    const uint32_t r = st.rank[i];
+    if (r < (uint32_t)kHeads) heads[r] = make_uint2(st.bits[i], (uint32_t)st.idx[i]);
+    st.rank[i] = 0u;
   }
 }
 

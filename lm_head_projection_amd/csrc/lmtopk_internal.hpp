@@ -56,6 +56,10 @@ int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* in
 // Largest LDS (bytes) one workgroup may use on the current device.
 int max_lds_per_block(size_t* bytes);
 
+// Upper bound of the static LDS of the chunk kernels (selection histograms
+// and the head staging); the dynamic LDS comes on top.
+constexpr size_t kChunkStaticLds = 40960;
+
 // LDS bytes the scoring kernels need.
 size_t binary_lds_bytes(int64_t M, int64_t H);
 size_t dense_lds_bytes(int64_t M, int chunk_rows);

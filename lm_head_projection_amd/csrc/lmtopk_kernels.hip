@@ -133,7 +133,7 @@ __device__ __forceinline__ void chunk_select_write(const float (&val)[RPL], cons
   for (int i = (int)n + (int)threadIdx.x; i < o.kc; i += blockDim.x)
     out[i] = make_uint2(0u, 0xFFFFFFFFu);
   lds_barrier();
-  if ((threadIdx.x >> 6) == 0) write_heads(st, n, o.heads + row_chunk * kHeads);
+  write_heads(st, n, o.heads + row_chunk * kHeads);
   if (!last) lds_barrier();  // the staging is refilled by the next row
 }
 
@@ -211,11 +211,18 @@ __device__ __forceinline__ void trit_dot(const uint4 (&w)[R], const uint4* tg, u
 // the weight loads).  In the steady state two quads are in flight while one
 // is computed; the loads are issued unconditionally and pinned in place so
 // that each wait covers only the buffer about to be used.
+static_assert(sizeof(SelectSmem) + sizeof(HeadStage) <= kChunkStaticLds,
+              "static LDS of the chunk kernels exceeds the bound the host checks");
+
+// Quads of weight loads in flight per wave.
+constexpr int kQuadBuffers = 2;
+
 template <int M, int R>
 __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs a) {
   extern __shared__ __align__(16) uint8_t dyn_lds[];
   __shared__ SelectSmem ssm;
   __shared__ HeadStage hst;
+  for (int i = threadIdx.x; i < kMaxK; i += blockDim.x) hst.rank[i] = 0u;  // ordered by the barriers below
   const int G = a.G;
   uint16_t* table = reinterpret_cast<uint16_t*>(dyn_lds);             // [256] trit codes
   TritGroup* tgs = reinterpret_cast<TritGroup*>(dyn_lds + 512);       // [M][G]
@@ -330,22 +337,22 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   // their masks
   lds_barrier();
 
-  // 4. first two quads of weights (group and quad indices clamped into the head)
-  //    (issued in the same order as the main loop's refills: all of quad 0,
-  //    then all of quad 1)
-  uint4 bufA[R][4], bufB[R][4];
-  float4 sA[R], sB[R];
+  // 4. first quads of weights (group and quad indices clamped into the head),
+  //    issued in the same order as the main loop's refills
+  uint4 buf[kQuadBuffers][R][4];
+  float4 sbuf[kQuadBuffers][R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    sA[r] = sp[r][0];
+  for (int b = 0; b < kQuadBuffers; ++b) {
+    const int qc = b < a.Q ? b : a.Q - 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bufA[r][i] = wp[r][(i < G ? i : G - 1) * 64];
-  }
+    for (int r = 0; r < R; ++r) {
+      sbuf[b][r] = sp[r][qc * 64];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    sB[r] = sp[r][(a.Q > 1 ? 1 : 0) * 64];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bufB[r][i] = wp[r][(4 + i < G ? 4 + i : G - 1) * 64];
+      for (int i = 0; i < 4; ++i) {
+        const int g = 4 * b + i;
+        buf[b][r][i] = wp[r][(g < G ? g : G - 1) * 64];
+      }
+    }
   }
 
   __builtin_amdgcn_sched_barrier(0);
@@ -392,24 +399,30 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   };
 
   if (active) {
-    // quads q (buffer A) and q + 1 (buffer B) are in flight at the top
+    // quads q .. q + kQuadBuffers - 1 are in flight at the top; each buffer is
+    // refilled right after its last use
+    constexpr int NB = kQuadBuffers;
     int q = 0;
-    for (; q + 3 < Qf; q += 2) {
-      compute_quad(q, bufA, sA);
-      __builtin_amdgcn_sched_barrier(0);  // keep each refill right after its buffer's last use
-      load_quad(q + 2, bufA, sA);
-      __builtin_amdgcn_sched_barrier(0);
-      compute_quad(q + 1, bufB, sB);
-      __builtin_amdgcn_sched_barrier(0);
-      load_quad(q + 3, bufB, sB);
-      __builtin_amdgcn_sched_barrier(0);
+    for (; q + 2 * NB - 1 < Qf; q += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        compute_quad(q + b, buf[b], sbuf[b]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_quad(q + b + NB, buf[b], sbuf[b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    if (q < Qf) {
-      compute_quad(q, bufA, sA);
-      if (q + 2 < Qf) load_quad(q + 2, bufA, sA);
+    // drain: fewer than 2 * NB quads remain
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (q + b < Qf) {
+        compute_quad(q + b, buf[b], sbuf[b]);
+        if (q + b + NB < Qf) load_quad(q + b + NB, buf[b], sbuf[b]);
+      }
     }
-    if (q + 1 < Qf) compute_quad(q + 1, bufB, sB);
-    if (q + 2 < Qf) compute_quad(q + 2, bufA, sA);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (q + NB + b < Qf) compute_quad(q + NB + b, buf[b], sbuf[b]);
     if (4 * Qf < G) {  // last, partial quad
       float4 st[R];
 #pragma unroll
@@ -488,6 +501,7 @@ __global__ __launch_bounds__(1024) void k_dense_chunk(DenseArgs a) {
   extern __shared__ __align__(16) uint8_t dyn_lds[];
   __shared__ SelectSmem ssm;
   __shared__ HeadStage hst;
+  for (int i = threadIdx.x; i < kMaxK; i += blockDim.x) hst.rank[i] = 0u;  // ordered by the barriers below
   float* scores = reinterpret_cast<float*>(dyn_lds);  // [M][C]
   const int C = a.chunk_rows;
   const int tid = threadIdx.x;
@@ -569,6 +583,7 @@ template <int RPL>
 __global__ __launch_bounds__(1024) void k_select_chunk(SelectArgs a) {
   __shared__ SelectSmem ssm;
   __shared__ HeadStage hst;
+  for (int i = threadIdx.x; i < kMaxK; i += blockDim.x) hst.rank[i] = 0u;  // ordered by the selection's barriers
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
   const int64_t base = (int64_t)blockIdx.x * a.chunk_rows;
@@ -661,7 +676,7 @@ namespace {
 template <typename Arg>
 hipError_t launch1(void (*kern)(Arg), dim3 grid, dim3 block, size_t lds, void* stream, Arg arg,
                    void* const* events = nullptr) {
-  if (lds > 32768) {  // with the kernel's static LDS the total may pass 64 KiB
+  if (lds + kChunkStaticLds > 65536) {  // with the static LDS the total may pass 64 KiB
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
