@@ -173,6 +173,22 @@ __device__ __forceinline__ uint32_t bcnt_acc(uint32_t x, uint32_t acc) {
   return r;
 }
 
+// Streaming loads of the head (and of logits on the selection-only path):
+// every byte is used once per call, so they are issued non-temporal (nt),
+// which keeps them from displacing other data in the caches and streams
+// faster from HBM than plain loads.
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float ld_stream(const float* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ float comp4(const float4& f, int i) {
   return i == 0 ? f.x : i == 1 ? f.y : i == 2 ? f.z : f.w;
 }
@@ -346,11 +362,11 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     const int qc = b < a.Q ? b : a.Q - 1;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      sbuf[b][r] = sp[r][qc * 64];
+      sbuf[b][r] = ld_stream(&sp[r][qc * 64]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int g = 4 * b + i;
-        buf[b][r][i] = wp[r][(g < G ? g : G - 1) * 64];
+        buf[b][r][i] = ld_stream(&wp[r][(g < G ? g : G - 1) * 64]);
       }
     }
   }
@@ -392,9 +408,9 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   auto load_quad = [&](int q, uint4 (&w)[R][4], float4 (&s)[R]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      s[r] = sp[r][q * 64];
+      s[r] = ld_stream(&sp[r][q * 64]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[r][i] = wp[r][(4 * q + i) * 64];
+      for (int i = 0; i < 4; ++i) w[r][i] = ld_stream(&wp[r][(4 * q + i) * 64]);
     }
   };
 
@@ -426,13 +442,13 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     if (4 * Qf < G) {  // last, partial quad
       float4 st[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) st[r] = sp[r][Qf * 64];
+      for (int r = 0; r < R; ++r) st[r] = ld_stream(&sp[r][Qf * 64]);
       for (int g = 4 * Qf; g < G; ++g) {
         uint4 w[R];
         float sc[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          w[r] = wp[r][g * 64];
+          w[r] = ld_stream(&wp[r][g * 64]);
           sc[r] = comp4(st[r], g - 4 * Qf);
         }
         compute_group(g, w, sc);
@@ -525,8 +541,8 @@ __global__ __launch_bounds__(1024) void k_dense_chunk(DenseArgs a) {
     const uint4* w1 = reinterpret_cast<const uint4*>(a.weight + (ok1 ? v1 : v0) * row_bytes);
 #pragma unroll 2
     for (int64_t i = lane; i < nvec; i += 64) {
-      const uint4 x0 = w0[i];
-      const uint4 x1 = w1[i];
+      const uint4 x0 = ld_stream(&w0[i]);
+      const uint4 x1 = ld_stream(&w1[i]);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const uint4 h = reinterpret_cast<const uint4*>(a.hidden + (int64_t)m * row_bytes)[i];
@@ -599,7 +615,7 @@ __global__ __launch_bounds__(1024) void k_select_chunk(SelectArgs a) {
     const float* row = a.logits + (size_t)m * a.ld;
     float val[RPL];
 #pragma unroll
-    for (int r = 0; r < RPL; ++r) val[r] = ((valid >> r) & 1u) ? row[idx[r]] : 0.f;
+    for (int r = 0; r < RPL; ++r) val[r] = ((valid >> r) & 1u) ? ld_stream(&row[idx[r]]) : 0.f;
     chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm, hst, m == (int)a.M - 1);
   }
 }
