@@ -302,30 +302,39 @@ __device__ uint32_t block_compact(const uint32_t (&key)[R], uint32_t valid, cons
   return selected;
 }
 
-// Chunk heads: besides its candidates in index order, every chunk writes its
-// kHeads best candidates in output order (value desc, index asc), padded with
-// index -1.  The merge reads only these heads unless a chunk may hold more
-// winners than its heads.
+// Chunk heads: besides its candidates, every chunk writes its kHeads best
+// candidates in output order (value desc, index asc), padded with index -1.
+// The merge reads only these heads unless a chunk may hold more winners than
+// its heads.
 constexpr int kHeads = 4;
 
-// The candidates of one chunk row as the compaction placed them (index order).
+// Small-k chunk selection (select_top_small) takes this many keys per wave.
+constexpr int kWaveTops = 4;
+// ... and gives up (the radix select runs) above this many survivors.
+constexpr uint32_t kSmallSurvivorsMax = 256;
+
+// LDS of the chunk selection's second stage: staged entries, their ranks and
+// the small-k path's per-wave tops.
 struct alignas(16) HeadStage {
+  uint32_t tops[kMaxWaves * kWaveTops];
   uint32_t key[kMaxK];
   uint32_t bits[kMaxK];
   int32_t idx[kMaxK];
   uint32_t rank[kMaxK];  // zero between uses
+  uint32_t wvalid[kMaxWaves];
+  uint32_t thr;
+  uint32_t count;
 };
 
-// The kHeads best of st[0, n) in output order -> heads[0, kHeads), padded
-// with index -1.  Every entry's position in the output order is the number of
-// entries ahead of it (greater key, or equal key and earlier staging position,
-// which is the lower index); the count for entry i is split over
-// blockDim / n threads and summed with LDS atomics; entries with a position
-// below kHeads write themselves.  Called by the whole workgroup; st.rank must
-// be zero on entry and is zero again on return.
-__device__ void write_heads(HeadStage& st, uint32_t n, uint2* heads) {
+__device__ __forceinline__ uint32_t wave_bound(uint32_t (&m)[4], int n_max, uint32_t k);
+
+// Output order of the staged entries st[0, n): rank[i] += the number of
+// entries ahead of entry i (greater key, or equal key and lower index).  The
+// count for entry i is split over blockDim / n threads and summed with LDS
+// atomics (integer adds, so the result does not depend on their order).  The
+// caller orders it with a barrier before reading st.rank.
+__device__ void stage_rank(HeadStage& st, uint32_t n) {
   const uint32_t tid = threadIdx.x, nt = blockDim.x;
-  if (tid >= n && tid < (uint32_t)kHeads) heads[tid] = make_uint2(0u, 0xFFFFFFFFu);
   if (n == 0) return;
   uint32_t segs = nt / n;
   segs = segs < 1u ? 1u : (segs > n ? n : segs);
@@ -335,19 +344,133 @@ __device__ void write_heads(HeadStage& st, uint32_t n, uint2* heads) {
     const uint32_t j0 = (t / n) * per;
     const uint32_t j1 = min(n, j0 + per);
     const uint32_t ki = st.key[i];
+    const int32_t ii = st.idx[i];
     uint32_t ahead = 0;
     for (uint32_t j = j0; j < j1; ++j) {
       const uint32_t kj = st.key[j];
-      ahead += (kj > ki || (kj == ki && j < i)) ? 1u : 0u;
+      ahead += (kj > ki || (kj == ki && st.idx[j] < ii)) ? 1u : 0u;
     }
     if (ahead) atomicAdd(&st.rank[i], ahead);
   }
+}
+
+// The kHeads best of st[0, n) in output order -> heads[0, kHeads), padded
+// with index -1.  Called by the whole workgroup; st.rank must be zero on
+// entry and is zero again on return.
+__device__ void write_heads(HeadStage& st, uint32_t n, uint2* heads) {
+  const uint32_t tid = threadIdx.x, nt = blockDim.x;
+  if (tid >= n && tid < (uint32_t)kHeads) heads[tid] = make_uint2(0u, 0xFFFFFFFFu);
+  if (n == 0) return;
+  stage_rank(st, n);
   lds_barrier();
   for (uint32_t i = tid; i < n; i += nt) {
     const uint32_t r = st.rank[i];
     if (r < (uint32_t)kHeads) heads[r] = make_uint2(st.bits[i], (uint32_t)st.idx[i]);
     st.rank[i] = 0u;
   }
+}
+
+// Exact top-k of one chunk row for small k (k <= kWaveTops * waves), without
+// radix passes.  Each wave takes its kWaveTops largest keys; the k-th largest
+// of these tops, T, is at most the chunk's k-th largest key (the tops are
+// real entries of the chunk), so every winner has key >= T.  The rows with
+// key >= T (typically a few more than k) are staged and ranked, and
+// out(pos, value_bits, index) is called for output positions pos <
+// min(k, valid rows), in no particular order of calls.  Returns that count,
+// or 0xFFFFFFFF (after writing nothing) when more than kSmallSurvivorsMax
+// rows pass T, e.g. with many equal keys.  Slot r of lane l in wave w is
+// position (w * R + r) * 64 + l as in block_select.  st.rank must be zero on
+// entry and is zero again on return.
+template <int R, typename Out>
+__device__ uint32_t select_top_small(const uint32_t (&key)[R], uint32_t valid,
+                                     const uint32_t (&vbits)[R], const int32_t (&index)[R],
+                                     uint32_t k, HeadStage& st, Out&& out) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int nw = blockDim.x >> 6;
+
+  // 1. this wave's kWaveTops largest keys (repeats count), 0 where absent
+  uint32_t left = valid, top = 0u, nvalid = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) nvalid += (uint32_t)__popcll(ballot((valid >> r) & 1u));
+#pragma unroll
+  for (int h = 0; h < kWaveTops; ++h) {
+    uint32_t best = 0u;
+    int br = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (((left >> r) & 1u) && key[r] > best) {
+        best = key[r];
+        br = r;
+      }
+    }
+    const uint32_t wm = wave_max_u32(best);
+    if (lane == h) top = wm;
+    if (wm == 0u) break;
+    const uint64_t holders = ballot(best == wm);
+    if (lane == __ffsll((long long)holders) - 1) left &= ~(1u << br);
+  }
+  if (lane < kWaveTops) st.tops[wave * kWaveTops + lane] = top;
+  if (lane == 0) st.wvalid[wave] = nvalid;
+  lds_barrier();
+
+  // 2. T, found by wave 0
+  if (wave == 0) {
+    const uint32_t c = lane < nw ? st.wvalid[lane] : 0u;
+    const uint32_t total = readlane_u32(row_scan_inclusive(c), 15);
+    uint32_t t = 1u;  // keeps every valid row (real keys are never 0)
+    if (total > k) {
+      // a key with at least k tops >= it (tops of short waves read as 0)
+      const int E = nw * kWaveTops;
+      uint32_t m4[4] = {lane < E ? st.tops[lane] : 0u, 0u, 0u, 0u};
+      const uint32_t b = wave_bound(m4, E, k);
+      if (b != 0u) t = b;  // else fewer than k real tops: keep every valid row
+    }
+    if (lane == 0) {
+      st.thr = t;
+      st.count = 0u;
+    }
+  }
+  lds_barrier();
+
+  // 3. stage the rows with key >= T (one atomic per wave reserves its slots)
+  const uint32_t t = st.thr;
+  uint64_t sv[R];
+  uint32_t nsv = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    sv[r] = ballot(((valid >> r) & 1u) && key[r] >= t);
+    nsv += (uint32_t)__popcll(sv[r]);
+  }
+  if (nsv) {
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&st.count, nsv);
+    base = readlane_u32(base, 0);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t p = base + lanes_below(sv[r]);
+      if (((sv[r] >> lane) & 1u) && p < kSmallSurvivorsMax) {
+        st.key[p] = key[r];
+        st.bits[p] = vbits[r];
+        st.idx[p] = index[r];
+      }
+      base += (uint32_t)__popcll(sv[r]);
+    }
+  }
+  lds_barrier();
+  const uint32_t n = st.count;
+  if (n > kSmallSurvivorsMax) return 0xFFFFFFFFu;
+
+  // 4. rank the staged rows and emit the first k
+  stage_rank(st, n);
+  lds_barrier();
+  for (uint32_t i = tid; i < n; i += blockDim.x) {
+    const uint32_t r = st.rank[i];
+    if (r < k) out(r, st.bits[i], st.idx[i]);
+    st.rank[i] = 0u;
+  }
+  return n < k ? n : k;
 }
 
 // LDS of the final merge: up to kMaxK entries to sort (4 slack entries so the

@@ -108,8 +108,11 @@ struct ChunkOut {
 };
 
 // Selects the chunk's top-k of row m from RPL slots per lane and writes them
-// (ascending index) followed by padding up to kc entries, then the chunk's
-// heads.  `last` = no further row follows in this workgroup.
+// followed by padding up to kc entries, then the chunk's heads.  Small k:
+// select_top_small, candidates in output order.  Otherwise (or when it gives
+// up): radix select, candidates in ascending index order.  Either order keeps
+// equal values in ascending index, which is all the merge relies on.  `last`
+// = no further row follows in this workgroup.
 template <int RPL>
 __device__ __forceinline__ void chunk_select_write(const float (&val)[RPL], const int32_t (&idx)[RPL],
                                                    uint32_t valid, int m, const ChunkOut& o,
@@ -120,9 +123,26 @@ __device__ __forceinline__ void chunk_select_write(const float (&val)[RPL], cons
     vb[r] = __float_as_uint(val[r]);
     key[r] = float_key(val[r]);
   }
-  const SelectRange s = block_select<RPL>(key, valid, (uint32_t)o.k, sm);
   const size_t row_chunk = (size_t)m * o.n_chunks + blockIdx.x;
   uint2* out = o.cand + row_chunk * o.kc;
+  uint2* heads = o.heads + row_chunk * kHeads;
+  if (o.k <= kWaveTops * (int)(blockDim.x >> 6)) {
+    const uint32_t n = select_top_small<RPL>(key, valid, vb, idx, (uint32_t)o.k, st,
+                                             [&](uint32_t pos, uint32_t bits, int32_t ix) {
+                                               const uint2 e = make_uint2(bits, (uint32_t)ix);
+                                               out[pos] = e;
+                                               if (pos < (uint32_t)kHeads) heads[pos] = e;
+                                             });
+    if (n != 0xFFFFFFFFu) {
+      for (int i = (int)n + (int)threadIdx.x; i < o.kc; i += blockDim.x)
+        out[i] = make_uint2(0u, 0xFFFFFFFFu);
+      for (int i = (int)n + (int)threadIdx.x; i < kHeads; i += blockDim.x)
+        heads[i] = make_uint2(0u, 0xFFFFFFFFu);
+      if (!last) lds_barrier();  // the staging is refilled by the next row
+      return;
+    }
+  }
+  const SelectRange s = block_select<RPL>(key, valid, (uint32_t)o.k, sm);
   const uint32_t n = block_compact<RPL>(key, valid, s, vb, idx, sm,
                                         [&](uint32_t pos, uint32_t bits, int32_t ix) {
                                           out[pos] = make_uint2(bits, (uint32_t)ix);
@@ -133,7 +153,7 @@ __device__ __forceinline__ void chunk_select_write(const float (&val)[RPL], cons
   for (int i = (int)n + (int)threadIdx.x; i < o.kc; i += blockDim.x)
     out[i] = make_uint2(0u, 0xFFFFFFFFu);
   lds_barrier();
-  write_heads(st, n, o.heads + row_chunk * kHeads);
+  write_heads(st, n, heads);
   if (!last) lds_barrier();  // the staging is refilled by the next row
 }
 

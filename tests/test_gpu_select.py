@@ -200,3 +200,15 @@ def test_merge_reads_whole_chunks_when_heads_may_not_suffice(layout):
         k = 200  # k-th best far below the chunk maxima: many chunks pass
     v, i = run_select(x, k, C)
     assert_select_exact(x, v, i, k)
+
+
+@pytest.mark.parametrize("V,k", [(3092, 50), (3172, 50), (3172, 64), (3172, 1), (4096 + 300, 64),
+                                 (1024 * 5 + 64, 8)])
+def test_small_k_chunk_path_ragged_tails(V, k):
+    # chunks of 1024 rows with k <= 64 take the per-wave-tops threshold; the
+    # last chunk here holds fewer rows than k, or few rows in few waves
+    x = synthetic.random_logits(3, V, seed=V + k, ties=0)
+    v, i = run_select(x, k, 1024)
+    assert_select_exact(x, v, i, k)
+    v2, i2 = run_select(x, k, 2048)
+    assert np.array_equal(i, i2)
