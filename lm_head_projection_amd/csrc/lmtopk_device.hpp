@@ -317,6 +317,9 @@ constexpr uint32_t kSmallSurvivorsMax = 256;
 // the small-k path's per-wave tops.
 struct alignas(16) HeadStage {
   uint32_t tops[kMaxWaves * kWaveTops];
+  uint32_t hkey[kMaxWaves * kHeads];  // block_heads: each wave's best entries
+  int32_t hidx[kMaxWaves * kHeads];
+  uint32_t hbits[kMaxWaves * kHeads];
   uint32_t key[kMaxK];
   uint32_t bits[kMaxK];
   int32_t idx[kMaxK];
@@ -354,19 +357,69 @@ __device__ void stage_rank(HeadStage& st, uint32_t n) {
   }
 }
 
-// The kHeads best of st[0, n) in output order -> heads[0, kHeads), padded
-// with index -1.  Called by the whole workgroup; st.rank must be zero on
-// entry and is zero again on return.
-__device__ void write_heads(HeadStage& st, uint32_t n, uint2* heads) {
-  const uint32_t tid = threadIdx.x, nt = blockDim.x;
-  if (tid >= n && tid < (uint32_t)kHeads) heads[tid] = make_uint2(0u, 0xFFFFFFFFu);
-  if (n == 0) return;
-  stage_rank(st, n);
+// The kHeads best valid entries of a chunk row in output order -> heads[0,
+// kHeads), padded with index -1, straight from the registers (slot layout as
+// in block_select).  Each wave takes its kHeads best (largest key, lowest
+// position among equal keys); wave 0 ranks the waves' entries by (key desc,
+// index asc).  Called by the whole workgroup; ends without a barrier.
+template <int R>
+__device__ void block_heads(const uint32_t (&key)[R], uint32_t valid, const uint32_t (&vbits)[R],
+                            const int32_t (&index)[R], HeadStage& st, uint2* heads) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  uint32_t left = valid;
+#pragma unroll
+  for (int h = 0; h < kHeads; ++h) {
+    uint32_t best = 0u;
+    int br = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (((left >> r) & 1u) && key[r] > best) {
+        best = key[r];
+        br = r;
+      }
+    }
+    const uint32_t wm = wave_max_u32(best);
+    const int slot = wave * kHeads + h;
+    if (wm == 0u) {  // fewer than h + 1 valid entries in this wave
+      if (lane == 0) {
+        st.hkey[slot] = 0u;
+        st.hidx[slot] = 0x7FFFFFFF;
+        st.hbits[slot] = 0u;
+      }
+      continue;
+    }
+    // among equal keys the lowest position (r * 64 + lane) is the lowest index
+    const uint32_t pmin = wave_min_u32(best == wm ? (uint32_t)(br * 64 + lane) : 0xFFFFFFFFu);
+    if ((uint32_t)(br * 64 + lane) == pmin && best == wm) {
+      st.hkey[slot] = wm;
+      st.hidx[slot] = index[br];
+      st.hbits[slot] = vbits[br];
+      left &= ~(1u << br);
+    }
+  }
   lds_barrier();
-  for (uint32_t i = tid; i < n; i += nt) {
-    const uint32_t r = st.rank[i];
-    if (r < (uint32_t)kHeads) heads[r] = make_uint2(st.bits[i], (uint32_t)st.idx[i]);
-    st.rank[i] = 0u;
+  if (wave == 0) {
+    const int E = nw * kHeads;
+    uint32_t e = 0u;
+    int32_t ei = 0x7FFFFFFF;
+    if (lane < E) {
+      e = st.hkey[lane];
+      ei = st.hidx[lane];
+    }
+    uint32_t rank = 0;
+    for (int q = 0; q < E; q += 4) {
+      const uint4 kq = *reinterpret_cast<const uint4*>(&st.hkey[q]);
+      const int4 iq = *reinterpret_cast<const int4*>(&st.hidx[q]);
+      rank += (kq.x > e || (kq.x == e && iq.x < ei)) ? 1u : 0u;
+      rank += (kq.y > e || (kq.y == e && iq.y < ei)) ? 1u : 0u;
+      rank += (kq.z > e || (kq.z == e && iq.z < ei)) ? 1u : 0u;
+      rank += (kq.w > e || (kq.w == e && iq.w < ei)) ? 1u : 0u;
+    }
+    // absent entries (key 0, index INT_MAX) rank after every real one
+    if (lane < E && rank < (uint32_t)kHeads)
+      heads[rank] = e != 0u ? make_uint2(st.hbits[lane], (uint32_t)ei) : make_uint2(0u, 0xFFFFFFFFu);
   }
 }
 

@@ -146,14 +146,12 @@ __device__ __forceinline__ void chunk_select_write(const float (&val)[RPL], cons
   const uint32_t n = block_compact<RPL>(key, valid, s, vb, idx, sm,
                                         [&](uint32_t pos, uint32_t bits, int32_t ix) {
                                           out[pos] = make_uint2(bits, (uint32_t)ix);
-                                          st.key[pos] = float_key(__uint_as_float(bits));
-                                          st.bits[pos] = bits;
-                                          st.idx[pos] = ix;
                                         });
   for (int i = (int)n + (int)threadIdx.x; i < o.kc; i += blockDim.x)
     out[i] = make_uint2(0u, 0xFFFFFFFFu);
-  lds_barrier();
-  write_heads(st, n, heads);
+  // the chunk's best entries are the best of its candidates (a head beyond
+  // a k < 4 is still a real logit of the row, which the merge may consider)
+  block_heads<RPL>(key, valid, vb, idx, st, heads);
   if (!last) lds_barrier();  // the staging is refilled by the next row
 }
 
