@@ -41,7 +41,8 @@ METRIC = "µs/token + achieved HBM GB/s, binary head V=248,320 H=5,120 k=50, M=1
 HBM_PEAK_GBPS = 8000.0
 SCORE_KERNEL = "k_binary_chunk"
 COPY_BYTES = 1 << 30
-KERNEL_SOURCES = ["lm_head_projection_amd/csrc/lmtopk_kernels.hip",
+KERNEL_SOURCES = ["lm_head_projection_amd/csrc/lmtopk_binary.hip",
+                  "lm_head_projection_amd/csrc/lmtopk_chunk.hpp",
                   "lm_head_projection_amd/csrc/lmtopk_device.hpp"]
 
 

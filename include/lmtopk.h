@@ -24,8 +24,10 @@
  *    fault inside a kernel surfaces at the caller's next synchronisation, as
  *    for any asynchronous HIP work.
  *  - The library keeps no state of its own and is thread safe.  A workspace
- *    needs no initialisation; every call overwrites what it reads.  Calls
- *    that share a workspace must be ordered on one stream.
+ *    must be zero-filled once before its first use (e.g. hipMemset after
+ *    hipMalloc); every call leaves its first 256 bytes zero again when it
+ *    completes and overwrites whatever else it reads.  Calls that share a
+ *    workspace must be ordered on one stream.
  *  - Inputs must be finite or +-inf.  NaN anywhere is outside the contract and
  *    gives an unspecified (but memory-safe) result.
  *  - +0.0 and -0.0 compare equal: they tie and the lower index comes first.
@@ -134,9 +136,12 @@ lmtopk_status lmtopk_packed_bytes(int64_t V, int64_t H, int32_t group_size,
 
 /* Host-only: workspace bytes needed by lmtopk_binary, lmtopk_dense and
    lmtopk_select for these sizes and options.  The same workspace serves all
-   three.  It holds, per row and chunk, the chunk's four best candidates and
-   all its candidates (8 bytes each), plus one intermediate merge level when
-   a row has more than 16384 candidates.
+   three.  It holds a 256-byte completion counter (zero between calls: the
+   workgroup that finishes a chunk launch last merges the candidates itself
+   when they fit it, instead of a second launch), then, per row and chunk,
+   the chunk's four best candidates and all its candidates (8 bytes each),
+   plus one intermediate merge level when a row has more than 16384
+   candidates.
    Errors: NULL, SHAPE, K, OPTIONS. */
 lmtopk_status lmtopk_workspace_bytes(int64_t M, int64_t V, int32_t k,
                                      const lmtopk_options* opt, size_t* bytes);

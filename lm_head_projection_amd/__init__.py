@@ -166,8 +166,9 @@ _WORKSPACES = {}
 
 
 def new_workspace(M, V, k, chunk_rows=0, device=None):
-    """A workspace for these sizes: uint8 on `device` (no initialisation needed)."""
-    return torch.empty(workspace_bytes(M, V, k, chunk_rows), dtype=torch.uint8, device=device)
+    """A workspace for these sizes: zero-filled uint8 on `device` (the library
+    keeps its first 256 bytes zero between calls)."""
+    return torch.zeros(workspace_bytes(M, V, k, chunk_rows), dtype=torch.uint8, device=device)
 
 
 def _workspace(dev, M, V, k, chunk_rows, workspace):
@@ -178,7 +179,7 @@ def _workspace(dev, M, V, k, chunk_rows, workspace):
         key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
         ws = _WORKSPACES.get(key)
         if ws is None or ws.numel() < need:
-            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            ws = torch.zeros(need, dtype=torch.uint8, device=dev)
             _WORKSPACES[key] = ws
         return ws
     _need_cuda("workspace", workspace, torch.uint8)

@@ -60,6 +60,7 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, Geome
   g->n_chunks = (int)((V + C - 1) / C);
   g->kc = k < C ? k : C;
   const int64_t n0 = (int64_t)g->n_chunks * g->kc;
+  g->sync_bytes = 256;
   g->heads_bytes = round_up((size_t)(M * g->n_chunks * 4 * 8), 256);
   g->region0_bytes = round_up((size_t)(M * n0 * 8), 256);
 
@@ -94,7 +95,14 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, Geome
     ++lv;
   }
   g->n_levels = lv;
-  g->workspace_bytes = g->heads_bytes + g->region0_bytes + g->region1_bytes;
+  // one merge level whose candidates fit the chunk workgroup: its last
+  // workgroup merges instead of a second launch
+  const int64_t chunk_threads = (int64_t)64 * g->nw;
+  if (lv == 1 && n0 <= chunk_threads * kFusedSlots) {
+    g->fused = 1;
+    g->n_levels = 0;
+  }
+  g->workspace_bytes = g->sync_bytes + g->heads_bytes + g->region0_bytes + g->region1_bytes;
   return LMTOPK_OK;
 }
 
@@ -203,8 +211,8 @@ lmtopk_status lmtopk_binary(const int8_t* act_q, const float* act_scale, const v
   if (lmtopk::max_lds_per_block(&lds_max)) return LMTOPK_ERR_HIP;
   if (lmtopk::binary_lds_bytes(M, H) + lmtopk::kChunkStaticLds > lds_max) return LMTOPK_ERR_SHAPE;
   const int e =
-      lmtopk::launch_binary_chunks(g, act_q, act_scale, wq, wscale, bias, H, workspace, stream,
-                                   score_events(opt));
+      lmtopk::launch_binary_chunks(g, act_q, act_scale, wq, wscale, bias, H, workspace, values,
+                                   indices, stream, score_events(opt));
   return finish(g, e, workspace, values, indices, stream);
 }
 
@@ -228,7 +236,7 @@ lmtopk_status lmtopk_dense(const void* hidden, const void* weight, lmtopk_dtype 
   if (lmtopk::dense_lds_bytes(M, g.chunk_rows) + lmtopk::kChunkStaticLds > lds_max)
     return LMTOPK_ERR_SHAPE;
   const int e = lmtopk::launch_dense_chunks(g, hidden, weight, dtype == LMTOPK_BF16, bias, H,
-                                            workspace, stream, score_events(opt));
+                                            workspace, values, indices, stream, score_events(opt));
   return finish(g, e, workspace, values, indices, stream);
 }
 
@@ -242,8 +250,8 @@ lmtopk_status lmtopk_select(const float* logits, int64_t M, int64_t V, int64_t l
   if (st) return st;
   if (ld < V) return LMTOPK_ERR_SHAPE;
   if (!lmtopk::aligned16(logits)) return LMTOPK_ERR_ALIGN;
-  const int e =
-      lmtopk::launch_select_chunks(g, logits, ld, workspace, stream, score_events(opt));
+  const int e = lmtopk::launch_select_chunks(g, logits, ld, workspace, values, indices, stream,
+                                             score_events(opt));
   return finish(g, e, workspace, values, indices, stream);
 }
 

@@ -1,0 +1,390 @@
+// lmtopk_binary.hip - binary-head chunk kernel (gfx950) and its launcher.
+//
+// k_binary_chunk: one workgroup scores one vocabulary chunk of a packed
+// binary head for all M rows, streaming every packed weight byte once, and
+// selects that chunk's exact top-k (lm-head-topk page, section "Method").
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+#include <stdint.h>
+
+#include "lmtopk_chunk.hpp"
+
+namespace lmtopk {
+
+constexpr int kGroup = 128;
+
+// Activations in balanced ternary.  Every int8 activation a is written as
+// a = sum_{p<6} 3^p d_p with digits d_p in {-1, 0, +1} (six trits reach
+// +-364).  For one group of 128 activations and trit p, two bit masks are
+// kept: NZ_p (d_p != 0) and POS_p (d_p == +1).  With the sign bits b of one
+// weight row (bit 1 = +1) the group's trit-p dot is
+//   sum_j sign_j d_pj = 2 popcount(XNOR(b, POS_p) AND NZ_p) - popcount(NZ_p),
+// so the exact integer group dot is
+//   D = sum_j a_j sign_j = 2 S - C,   S = sum_p 3^p popcount(XNOR(b, POS_p) AND NZ_p),
+//   C = sum_p 3^p popcount(NZ_p)  (the same for every weight row).
+// Per 32 weights and trit that is one 3-input bit operation (v_bitop3) and
+// one accumulating popcount (v_bcnt), 48 + 5 Horner steps per group of 128.
+struct TritGroup {
+  uint4 pos_nz[12];  // [trit p] -> {POS_p, NZ_p}, 4 words = 128 activations each
+};
+
+struct BinaryArgs {
+  const int8_t* act_q;     // [M][H]
+  const float* act_scale;  // [M]
+  const uint4* wq;         // packed signs, layout v1
+  const float4* wscale;    // packed scales, layout v1
+  const float* bias;       // [V] or null
+  int64_t V, H, n_tiles;
+  int G, Q;
+  int tiles_per_chunk;
+  ChunkOut out;
+};
+
+__device__ __forceinline__ uint32_t bcnt_acc(uint32_t x, uint32_t acc) {
+  uint32_t r;
+  asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(acc));
+  return r;
+}
+
+__device__ __forceinline__ float comp4(const float4& f, int i) {
+  return i == 0 ? f.x : i == 1 ? f.y : i == 2 ? f.z : f.w;
+}
+
+// S of one group for R weight rows at once: the trit masks are read once and
+// serve all R rows.
+template <int R>
+__device__ __forceinline__ void trit_dot(const uint4 (&w)[R], const uint4* tg, uint32_t (&u)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) u[r] = 0u;
+#pragma unroll
+  for (int p = 5; p >= 0; --p) {
+    const uint4 pos = tg[2 * p];
+    const uint4 nz = tg[2 * p + 1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint32_t x = (u[r] << 1) + u[r];
+      x = bcnt_acc(~(w[r].x ^ pos.x) & nz.x, x);
+      x = bcnt_acc(~(w[r].y ^ pos.y) & nz.y, x);
+      x = bcnt_acc(~(w[r].z ^ pos.z) & nz.z, x);
+      x = bcnt_acc(~(w[r].w ^ pos.w) & nz.w, x);
+      u[r] = x;
+    }
+  }
+}
+
+// Lane l of wave w owns the R rows ((chunk * tiles_per_chunk + w * R + r) * 64 + l),
+// r < R, and scores them together.  Each group's 128 sign bits of a row are
+// one 16-byte load; the four scales of a quad of groups are one more.  The
+// fp32 logit accumulates fmaf((float)D_g, scale_g, acc) in ascending g, so
+// every row takes the same operation sequence wherever it sits.
+//
+// Latency: the activation bytes are requested first and the first two quads
+// of weights right after them; the trit masks are built while those weights
+// are in flight (the barriers here only order LDS, so they do not wait for
+// the weight loads).  In the steady state two quads are in flight while one
+// is computed; the loads are issued unconditionally and pinned in place so
+// that each wait covers only the buffer about to be used.
+static_assert(sizeof(SelectSmem) + sizeof(ChunkSmem) + 16 <= kChunkStaticLds,
+              "static LDS of the chunk kernels exceeds the bound the host checks");
+
+// Quads of weight loads in flight per wave.
+constexpr int kQuadBuffers = 2;
+
+template <int M, int R>
+__global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs a) {
+  extern __shared__ __align__(16) uint8_t dyn_lds[];
+  __shared__ SelectSmem ssm;
+  __shared__ ChunkSmem csm;
+  __shared__ uint32_t last_wg;
+  HeadStage& hst = csm.hs;
+  for (int i = threadIdx.x; i < kMaxK; i += blockDim.x) hst.rank[i] = 0u;  // ordered by the barriers below
+  const int G = a.G;
+  uint16_t* table = reinterpret_cast<uint16_t*>(dyn_lds);             // [256] trit codes
+  TritGroup* tgs = reinterpret_cast<TritGroup*>(dyn_lds + 512);       // [M][G]
+  int* cg = reinterpret_cast<int*>(tgs + (size_t)M * G);              // [M][G] C of the group
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int nw = blockDim.x >> 6;
+  const int Qf = G >> 2;  // full quads
+  const int64_t tile0 = (int64_t)blockIdx.x * a.tiles_per_chunk + (int64_t)wave * R;
+  const bool active = tile0 < a.n_tiles;
+
+  // a tile past the last one reads the last tile; its rows are never offered
+  const uint4* wp[R];
+  const float4* sp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t t = tile0 + r < a.n_tiles ? tile0 + r : a.n_tiles - 1;
+    wp[r] = a.wq + (size_t)t * G * 64 + lane;
+    sp[r] = a.wscale + (size_t)t * a.Q * 64 + lane;
+  }
+
+  // Prologue.  Everything whose load count depends on the shapes happens
+  // before the weight prefetch, and the prefetch is followed only by
+  // straight-line code, so the waits after it cover exactly what they need.
+  // 1. trit code of every int8 value: bits 0..5 NZ_p, bits 8..13 POS_p
+  for (int e = tid; e < 256; e += blockDim.x) {
+    int v = e < 128 ? e : e - 256;
+    uint32_t c = 0u;
+#pragma unroll
+    for (int p = 0; p < 6; ++p) {
+      int r = v % 3;  // in {-2, ..., 2}
+      if (r == 2) r = -1;
+      if (r == -2) r = 1;
+      if (r != 0) c |= 1u << p;
+      if (r == 1) c |= 1u << (8 + p);
+      v = (v - r) / 3;
+    }
+    table[e] = (uint16_t)c;
+  }
+  lds_barrier();
+
+  // 2. trit masks of a batch of groups: each mask word is one ballot over 64
+  //    activations (groups b0, b0 + nw, ..., this wave's share)
+  constexpr int kBatch = 4;
+  const int n_mg = M * G;
+  auto load_acts = [&](int b0, int8_t (&y0)[kBatch], int8_t (&y1)[kBatch]) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      int mg = b0 + i * nw;
+      mg = mg < n_mg ? mg : n_mg - 1;  // clamped; the extra groups are not used
+      const int m = mg / G;
+      const int8_t* src = a.act_q + (size_t)m * a.H + (size_t)(mg - m * G) * kGroup;
+      y0[i] = src[lane];
+      y1[i] = src[64 + lane];
+    }
+  };
+  auto build_masks = [&](int b0, const int8_t (&y0)[kBatch], const int8_t (&y1)[kBatch]) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int mg = b0 + i * nw;
+      if (mg >= n_mg) break;
+      const uint32_t c0 = table[(uint8_t)y0[i]];
+      const uint32_t c1 = table[(uint8_t)y1[i]];
+      uint4 mine = make_uint4(0u, 0u, 0u, 0u);
+      int cgroup = 0, w3 = 1;
+#pragma unroll
+      for (int p = 0; p < 6; ++p) {
+        const uint64_t p0 = ballot((c0 >> (8 + p)) & 1u), p1 = ballot((c1 >> (8 + p)) & 1u);
+        const uint64_t n0 = ballot((c0 >> p) & 1u), n1 = ballot((c1 >> p) & 1u);
+        if (lane == 2 * p)
+          mine = make_uint4((uint32_t)p0, (uint32_t)(p0 >> 32), (uint32_t)p1, (uint32_t)(p1 >> 32));
+        if (lane == 2 * p + 1)
+          mine = make_uint4((uint32_t)n0, (uint32_t)(n0 >> 32), (uint32_t)n1, (uint32_t)(n1 >> 32));
+        cgroup += w3 * (__popcll(n0) + __popcll(n1));
+        w3 *= 3;
+      }
+      if (lane < 12) tgs[mg].pos_nz[lane] = mine;
+      if (lane == 0) cg[mg] = cgroup;
+    }
+  };
+  //    batches after the first (large M * H only)
+  for (int b0 = wave + nw * kBatch; b0 < n_mg; b0 += nw * kBatch) {
+    int8_t y0[kBatch], y1[kBatch];
+    load_acts(b0, y0, y1);
+    build_masks(b0, y0, y1);
+  }
+  // 3. the first batch's activation bytes, this lane's bias and the row
+  //    scales (loaded now: after the main loop a load would cost a full
+  //    memory round trip in the tail)
+  int8_t x0[kBatch], x1[kBatch];
+  load_acts(wave, x0, x1);
+  float bias_v[R];
+  {
+    // unconditional loads from valid addresses; the values are used only
+    // for real rows of a real bias
+    const float* bp = a.bias != nullptr ? a.bias : a.act_scale;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      int64_t v = (tile0 + r) * 64 + lane;
+      v = a.bias != nullptr ? (v < a.V ? v : a.V - 1) : 0;
+      bias_v[r] = bp[v];
+    }
+  }
+  float act_s[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) act_s[m] = a.act_scale[m];
+  __builtin_amdgcn_sched_barrier(0);
+  // every wave's activation requests go out before any wave's weight
+  // requests: the CU serves its requests in order, so otherwise the last
+  // waves would wait for most of the weight prefetch before they could build
+  // their masks
+  lds_barrier();
+
+  // 4. first quads of weights (group and quad indices clamped into the head),
+  //    issued in the same order as the main loop's refills
+  uint4 buf[kQuadBuffers][R][4];
+  float4 sbuf[kQuadBuffers][R];
+#pragma unroll
+  for (int b = 0; b < kQuadBuffers; ++b) {
+    const int qc = b < a.Q ? b : a.Q - 1;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      sbuf[b][r] = ld_stream(&sp[r][qc * 64]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = 4 * b + i;
+        buf[b][r][i] = ld_stream(&wp[r][(g < G ? g : G - 1) * 64]);
+      }
+    }
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  // 5. the first batch's masks, built while the weights are in flight
+  build_masks(wave, x0, x1);
+  lds_barrier();
+
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+
+  auto compute_group = [&](int g, const uint4 (&w)[R], const float (&s)[R]) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      uint32_t u[R];
+      trit_dot<R>(w, tgs[(size_t)m * G + g].pos_nz, u);
+      const int c = cg[m * G + g];
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r][m] = fmaf((float)(2 * (int)u[r] - c), s[r], acc[r][m]);
+    }
+  };
+  auto compute_quad = [&](int q, const uint4 (&buf)[R][4], const float4 (&s)[R]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 w[R];
+      float sc[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        w[r] = buf[r][i];
+        sc[r] = comp4(s[r], i);
+      }
+      compute_group(4 * q + i, w, sc);
+    }
+  };
+  auto load_quad = [&](int q, uint4 (&w)[R][4], float4 (&s)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      s[r] = ld_stream(&sp[r][q * 64]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[r][i] = ld_stream(&wp[r][(4 * q + i) * 64]);
+    }
+  };
+
+  if (active) {
+    // quads q .. q + kQuadBuffers - 1 are in flight at the top; each buffer is
+    // refilled right after its last use
+    constexpr int NB = kQuadBuffers;
+    int q = 0;
+    for (; q + 2 * NB - 1 < Qf; q += NB) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        compute_quad(q + b, buf[b], sbuf[b]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_quad(q + b + NB, buf[b], sbuf[b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // drain: fewer than 2 * NB quads remain
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (q + b < Qf) {
+        compute_quad(q + b, buf[b], sbuf[b]);
+        if (q + b + NB < Qf) load_quad(q + b + NB, buf[b], sbuf[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (q + NB + b < Qf) compute_quad(q + NB + b, buf[b], sbuf[b]);
+    if (4 * Qf < G) {  // last, partial quad
+      float4 st[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) st[r] = ld_stream(&sp[r][Qf * 64]);
+      for (int g = 4 * Qf; g < G; ++g) {
+        uint4 w[R];
+        float sc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          w[r] = ld_stream(&wp[r][g * 64]);
+          sc[r] = comp4(st[r], g - 4 * Qf);
+        }
+        compute_group(g, w, sc);
+      }
+    }
+  }
+
+  int32_t idx[R];
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t v = (tile0 + r) * 64 + lane;
+    idx[r] = (int32_t)v;
+    const bool vv = (tile0 + r) < a.n_tiles && v < a.V;
+    valid |= (vv ? 1u : 0u) << r;
+    if (a.bias == nullptr || !vv) bias_v[r] = 0.f;
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const float s = act_s[m];
+    float val[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) val[r] = fmaf(acc[r][m], s, bias_v[r]);
+    chunk_select_write<R>(val, idx, valid, m, a.out, ssm, hst, m == M - 1);
+  }
+  if (a.out.fused) fused_merge_tail<kFusedRM>(a.out.merge, ssm, csm.fs, last_wg);
+}
+namespace {
+
+template <int M>
+void (*binary_kernel_m(int rpl))(BinaryArgs) {
+  switch (rpl) {
+    case 1: return k_binary_chunk<M, 1>;
+    case 4: return k_binary_chunk<M, 4>;
+  }
+  return nullptr;
+}
+
+void (*binary_kernel(int M, int rpl))(BinaryArgs) {
+  switch (M) {
+    case 1: return binary_kernel_m<1>(rpl);
+    case 2: return binary_kernel_m<2>(rpl);
+    case 3: return binary_kernel_m<3>(rpl);
+    case 4: return binary_kernel_m<4>(rpl);
+    case 5: return binary_kernel_m<5>(rpl);
+    case 6: return binary_kernel_m<6>(rpl);
+    case 7: return binary_kernel_m<7>(rpl);
+    case 8: return binary_kernel_m<8>(rpl);
+  }
+  return nullptr;
+}
+}  // namespace
+
+size_t binary_lds_bytes(int64_t M, int64_t H) {
+  const int64_t G = H / kGroup;
+  return (size_t)(512 + M * G * sizeof(TritGroup) + M * G * 4);
+}
+int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* act_scale,
+                         const void* wq, const float* wscale, const float* bias, int64_t H,
+                         void* workspace, float* values, int64_t* indices, void* stream,
+                         void* const* events) {
+  BinaryArgs a;
+  a.act_q = act_q;
+  a.act_scale = act_scale;
+  a.wq = static_cast<const uint4*>(wq);
+  a.wscale = reinterpret_cast<const float4*>(wscale);
+  a.bias = bias;
+  a.V = g.V;
+  a.H = H;
+  a.n_tiles = g.n_tiles;
+  a.G = (int)(H / kGroup);
+  a.Q = (a.G + 3) / 4;
+  a.tiles_per_chunk = g.chunk_rows / 64;
+  a.out = chunk_out(g, workspace, values, indices);
+  auto kern = binary_kernel((int)g.M, g.rpl);
+  if (!kern) return (int)hipErrorInvalidValue;
+  return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), binary_lds_bytes(g.M, H), stream, a,
+                      events);
+}
+}  // namespace lmtopk

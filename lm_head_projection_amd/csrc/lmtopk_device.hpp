@@ -56,6 +56,12 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// A value the whole wave shares, marked as such for the compiler (scalar
+// register), e.g. the wave index or a count read from LDS: loops and
+// branches on it stay uniform instead of becoming per-lane.
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int wave_id() { return (int)uniform(threadIdx.x >> 6); }
+
 __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }
@@ -120,6 +126,23 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Candidate lists and chunk heads are written by every chunk workgroup and,
+// on the fused path, read back by the last workgroup of the same launch,
+// which may sit on another XCD with its own L2.  They are therefore accessed
+// with device-scope (agent) atomic loads and stores: on gfx950 these are
+// plain 8-byte vector loads and stores whose scope bits make the store write
+// through the XCD's L2 and the load fetch past it, so no cache write-back
+// fence is needed.
+__device__ __forceinline__ void st_cand(uint2* p, uint2 v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), ((uint64_t)v.y << 32) | (uint64_t)v.x,
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint2 ld_cand(const uint2* p) {
+  const uint64_t x = __hip_atomic_load(const_cast<uint64_t*>(reinterpret_cast<const uint64_t*>(p)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2((uint32_t)x, (uint32_t)(x >> 32));
+}
+
 // LDS used by one selection (any number of sequential selections may reuse it).
 struct alignas(16) SelectSmem {
   uint32_t hist[3][256];
@@ -149,7 +172,7 @@ __device__ SelectRange block_select(const uint32_t (&key)[R], uint32_t valid, ui
                                     SelectSmem& sm) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int nw = blockDim.x >> 6;
 
   // histogram buffers 0 and 1 start clean; buffer 2 is cleared in pass 0
@@ -257,7 +280,7 @@ __device__ uint32_t block_compact(const uint32_t (&key)[R], uint32_t valid, cons
                                   SelectSmem& sm, Sink&& sink) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int nw = blockDim.x >> 6;
   bool gt[R], eq[R];
   uint32_t ngt = 0, neq = 0;
@@ -317,6 +340,7 @@ constexpr uint32_t kSmallSurvivorsMax = 256;
 // the small-k path's per-wave tops.
 struct alignas(16) HeadStage {
   uint32_t tops[kMaxWaves * kWaveTops];
+  uint32_t trank[kMaxWaves * kWaveTops];  // ranks of the tops, zero between uses
   uint32_t hkey[kMaxWaves * kHeads];  // block_heads: each wave's best entries
   int32_t hidx[kMaxWaves * kHeads];
   uint32_t hbits[kMaxWaves * kHeads];
@@ -329,31 +353,39 @@ struct alignas(16) HeadStage {
   uint32_t count;
 };
 
-__device__ __forceinline__ uint32_t wave_bound(uint32_t (&m)[4], int n_max, uint32_t k);
-
-// Output order of the staged entries st[0, n): rank[i] += the number of
-// entries ahead of entry i (greater key, or equal key and lower index).  The
-// count for entry i is split over blockDim / n threads and summed with LDS
-// atomics (integer adds, so the result does not depend on their order).  The
-// caller orders it with a barrier before reading st.rank.
-__device__ void stage_rank(HeadStage& st, uint32_t n) {
-  const uint32_t tid = threadIdx.x, nt = blockDim.x;
-  if (n == 0) return;
-  uint32_t segs = nt / n;
-  segs = segs < 1u ? 1u : (segs > n ? n : segs);
-  const uint32_t per = (n + segs - 1u) / segs;
-  for (uint32_t t = tid; t < n * segs; t += nt) {
-    const uint32_t i = t % n;
-    const uint32_t j0 = (t / n) * per;
-    const uint32_t j1 = min(n, j0 + per);
-    const uint32_t ki = st.key[i];
-    const int32_t ii = st.idx[i];
-    uint32_t ahead = 0;
-    for (uint32_t j = j0; j < j1; ++j) {
-      const uint32_t kj = st.key[j];
-      ahead += (kj > ki || (kj == ki && st.idx[j] < ii)) ? 1u : 0u;
-    }
-    if (ahead) atomicAdd(&st.rank[i], ahead);
+// rank[i] += the number of entries ahead of entry i among n entries in LDS:
+// greater key, or equal key and lower idx (idx == nullptr: lower position).
+// The work is spread over every wave of the workgroup: job (slice s, block
+// b) compares the 64 entries of block b with the four entries of slice s,
+// read as one LDS broadcast, and adds the counts with one LDS atomic per
+// entry (integer adds, so the result does not depend on their order).  key
+// and idx must be readable up to index 4 * ceil(n / 4); rank[0, n) must be
+// zero on entry; the caller orders the result with a barrier.
+__device__ __forceinline__ void rank_count(const uint32_t* key, const int32_t* idx, uint32_t n,
+                                           uint32_t* rank) {
+  n = uniform(n);
+  if (n == 0u) return;
+  const int lane = lane_id();
+  const uint32_t wave = (uint32_t)wave_id(), nw = blockDim.x >> 6;
+  const uint32_t nb = (n + 63u) >> 6;
+  const uint32_t ns = (n + 3u) >> 2;
+  for (uint32_t job = wave; job < ns * nb; job += nw) {
+    const uint32_t sl = job % ns, b = job / ns;
+    const uint32_t j0 = sl * 4u;
+    const uint32_t i = b * 64u + (uint32_t)lane;
+    const bool vi = i < n;
+    const uint32_t ki = vi ? key[i] : 0u;
+    const int32_t ii = vi ? (idx ? idx[i] : (int32_t)i) : 0;
+    const uint4 kq = *reinterpret_cast<const uint4*>(&key[j0]);
+    const int4 iq = idx ? *reinterpret_cast<const int4*>(&idx[j0])
+                        : make_int4((int)j0, (int)j0 + 1, (int)j0 + 2, (int)j0 + 3);
+    const uint32_t kj[4] = {kq.x, kq.y, kq.z, kq.w};
+    const int32_t ij[4] = {iq.x, iq.y, iq.z, iq.w};
+    uint32_t c = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      c += (j0 + e < n && (kj[e] > ki || (kj[e] == ki && ij[e] < ii))) ? 1u : 0u;
+    if (vi && c) atomicAdd(&rank[i], c);
   }
 }
 
@@ -366,7 +398,7 @@ template <int R>
 __device__ void block_heads(const uint32_t (&key)[R], uint32_t valid, const uint32_t (&vbits)[R],
                             const int32_t (&index)[R], HeadStage& st, uint2* heads) {
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int nw = blockDim.x >> 6;
   uint32_t left = valid;
 #pragma unroll
@@ -419,7 +451,7 @@ __device__ void block_heads(const uint32_t (&key)[R], uint32_t valid, const uint
     }
     // absent entries (key 0, index INT_MAX) rank after every real one
     if (lane < E && rank < (uint32_t)kHeads)
-      heads[rank] = e != 0u ? make_uint2(st.hbits[lane], (uint32_t)ei) : make_uint2(0u, 0xFFFFFFFFu);
+      st_cand(&heads[rank], e != 0u ? make_uint2(st.hbits[lane], (uint32_t)ei) : make_uint2(0u, 0xFFFFFFFFu));
   }
 }
 
@@ -433,14 +465,15 @@ __device__ void block_heads(const uint32_t (&key)[R], uint32_t valid, const uint
 // or 0xFFFFFFFF (after writing nothing) when more than kSmallSurvivorsMax
 // rows pass T, e.g. with many equal keys.  Slot r of lane l in wave w is
 // position (w * R + r) * 64 + l as in block_select.  st.rank must be zero on
-// entry and is zero again on return.
+// entry and is zero again on return.  Four barriers: after the tops, after
+// their ranks, after the staging, after the ranks of the staged rows.
 template <int R, typename Out>
 __device__ uint32_t select_top_small(const uint32_t (&key)[R], uint32_t valid,
                                      const uint32_t (&vbits)[R], const int32_t (&index)[R],
                                      uint32_t k, HeadStage& st, Out&& out) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int nw = blockDim.x >> 6;
 
   // 1. this wave's kWaveTops largest keys (repeats count), 0 where absent
@@ -466,29 +499,25 @@ __device__ uint32_t select_top_small(const uint32_t (&key)[R], uint32_t valid,
   }
   if (lane < kWaveTops) st.tops[wave * kWaveTops + lane] = top;
   if (lane == 0) st.wvalid[wave] = nvalid;
+  if (tid == 0) st.count = 0u;
+  for (int i = tid; i < kMaxWaves * kWaveTops; i += (int)blockDim.x) st.trank[i] = 0u;
   lds_barrier();
 
-  // 2. T, found by wave 0
-  if (wave == 0) {
-    const uint32_t c = lane < nw ? st.wvalid[lane] : 0u;
-    const uint32_t total = readlane_u32(row_scan_inclusive(c), 15);
-    uint32_t t = 1u;  // keeps every valid row (real keys are never 0)
-    if (total > k) {
-      // a key with at least k tops >= it (tops of short waves read as 0)
-      const int E = nw * kWaveTops;
-      uint32_t m4[4] = {lane < E ? st.tops[lane] : 0u, 0u, 0u, 0u};
-      const uint32_t b = wave_bound(m4, E, k);
-      if (b != 0u) t = b;  // else fewer than k real tops: keep every valid row
-    }
-    if (lane == 0) {
-      st.thr = t;
-      st.count = 0u;
-    }
-  }
+  // 2. T = the k-th largest top (ties broken by position), when more than k
+  //    rows are valid
+  const int E = nw * kWaveTops;  // <= 64
+  const uint32_t c = lane < nw ? st.wvalid[lane] : 0u;
+  const uint32_t total = readlane_u32(row_scan_inclusive(c), 15);
+  if (total > k) rank_count(st.tops, nullptr, (uint32_t)E, st.trank);
   lds_barrier();
 
   // 3. stage the rows with key >= T (one atomic per wave reserves its slots)
-  const uint32_t t = st.thr;
+  uint32_t t = 1u;  // keeps every valid row (real keys are never 0)
+  if (total > k) {
+    const uint64_t at = ballot(lane < E && st.trank[lane] == k - 1u);
+    const uint32_t b = readlane_u32(lane < E ? st.tops[lane] : 0u, at ? __ffsll((long long)at) - 1 : 0);
+    if (b != 0u) t = b;  // else fewer than k real tops: keep every valid row
+  }
   uint64_t sv[R];
   uint32_t nsv = 0;
 #pragma unroll
@@ -512,11 +541,11 @@ __device__ uint32_t select_top_small(const uint32_t (&key)[R], uint32_t valid,
     }
   }
   lds_barrier();
-  const uint32_t n = st.count;
+  const uint32_t n = uniform(st.count);
   if (n > kSmallSurvivorsMax) return 0xFFFFFFFFu;
 
   // 4. rank the staged rows and emit the first k
-  stage_rank(st, n);
+  rank_count(st.key, st.idx, n, st.rank);
   lds_barrier();
   for (uint32_t i = tid; i < n; i += blockDim.x) {
     const uint32_t r = st.rank[i];
@@ -537,6 +566,9 @@ struct alignas(16) FinalSmem {
   uint32_t bound;   // survivor threshold (a key)
   uint32_t n_over;  // chunks whose heads may not hold all their survivors
   int32_t over[256];
+  uint32_t wmin[kMaxWaves];
+  uint32_t wmax[kMaxWaves];
+  uint32_t hist[256];  // chunk maxima per 8-bit digit
 };
 
 // Entries [0, n) of fs are filled, [n, 4 * ceil(n / 4)) hold padding that is
@@ -545,7 +577,7 @@ struct alignas(16) FinalSmem {
 // and lower index).  The count for entry i is split over up to
 // blockDim / n threads, each scanning one segment of the entries, and summed
 // with LDS atomics (integer adds: the result does not depend on their order).
-__device__ void rank_and_write(FinalSmem& fs, uint32_t n, uint32_t k, float* values,
+__device__ __forceinline__ void rank_and_write(FinalSmem& fs, uint32_t n, uint32_t k, float* values,
                                int64_t* indices) {
   if (n == 0) return;
   const uint32_t nq = (n + 3u) >> 2;
@@ -577,57 +609,6 @@ __device__ void rank_and_write(FinalSmem& fs, uint32_t n, uint32_t k, float* val
       indices[rank] = (int64_t)fs.idx[i];
     }
   }
-}
-
-// Survivor threshold from the chunk maxima held by one wave (m[r] of lane l is
-// chunk r * 64 + l; chunks >= n_max are absent; k <= n_max <= 256).  Returns a
-// key T such that at least k of the maxima are >= T, so T is at most the k-th
-// largest maximum.  MSB-first search for the k-th largest, one bit per step
-// below the bits all maxima share; it stops as soon as the keys that share
-// the prefix found so far are exactly the ones still needed, or once bit
-// kBoundLowBit is decided (a coarser T only lets a few more candidates pass).
-constexpr int kBoundLowBit = 16;
-
-__device__ __forceinline__ uint32_t wave_bound(uint32_t (&m)[4], int n_max, uint32_t k) {
-  const int lane = lane_id();
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (r * 64 + lane < n_max) {
-      lo = min(lo, m[r]);
-      hi = max(hi, m[r]);
-    }
-  }
-  lo = wave_min_u32(lo);
-  hi = wave_max_u32(hi);
-  if (lo == hi) return lo;
-  // absent chunks become copies of the smallest maximum: with k <= n_max
-  // that leaves every bound >= lo unchanged, and any T <= lo is valid anyway
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    if (r * 64 + lane >= n_max) m[r] = lo;
-  const int common = __clz(lo ^ hi);
-  uint32_t mask = common ? (0xFFFFFFFFu << (32 - common)) : 0u;
-  uint32_t prefix = hi & mask;
-  uint32_t need = k;      // keys still needed from the current range
-  uint32_t inside = 256;  // keys in the current range
-  for (int bit = 31 - common; bit >= kBoundLowBit; --bit) {
-    const uint32_t mb = mask | (1u << bit);
-    const uint32_t pb = prefix | (1u << bit);
-    uint32_t upper = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) upper += (uint32_t)__popcll(ballot((m[r] & mb) == pb));
-    if (upper >= need) {
-      prefix = pb;
-      inside = upper;
-    } else {
-      need -= upper;
-      inside -= upper;
-    }
-    mask = mb;
-    if (inside == need) break;
-  }
-  return prefix;
 }
 
 // Puts this lane's entry into the survivor list if `take`: one LDS atomic per
@@ -666,56 +647,81 @@ __device__ __forceinline__ void place_survivor(FinalSmem& fs, bool take, uint32_
 // are ranked there.  With too many chunks or survivors, the radix select of
 // all candidates runs instead.
 template <int RM>
-__device__ void merge_final(const uint2* in, int64_t n_in, const uint2* heads, int n_max, int kc,
+__device__ __forceinline__ void merge_final(const uint2* in, int64_t n_in, const uint2* heads, int n_max, int kc,
                             uint32_t k, float* values, int64_t* indices, int nthreads,
                             SelectSmem& sm, FinalSmem& fs) {
   // nthreads == blockDim.x, passed in so that no load of it queues behind
   // the data loads
   const int tid = threadIdx.x;
   const int lane = lane_id();
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int n_heads = n_max * kHeads;
 
   for (int i = tid; i < kMaxK + 4; i += nthreads) fs.rank[i] = 0u;
 
   if (heads != nullptr && n_max >= (int)k && n_max <= 256 && n_heads <= nthreads) {
-    // Loads are unconditional (indices clamped into the arrays) so that all
-    // of them are in flight at once; the maxima go first, the bound waits
-    // only for them.
-    uint32_t m[4] = {0u, 0u, 0u, 0u};
-    if (wave == 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = min(r * 64 + lane, n_max - 1);
-        m[r] = float_key(__uint_as_float(heads[(size_t)c * kHeads].x));
-      }
-    }
+    // Every thread loads one head and the last head of that head's chunk,
+    // unconditionally (indices clamped into the arrays), so all loads are in
+    // flight at once; thread 4c holds chunk c's maximum.
     const int e = min(tid, n_heads - 1);
     const int c = e / kHeads;
-    const uint2 he = heads[e];
-    const uint2 hl = heads[(size_t)c * kHeads + (kHeads - 1)];
+    const uint2 he = ld_cand(&heads[e]);
+    const uint2 hl = ld_cand(&heads[(size_t)c * kHeads + (kHeads - 1)]);
     for (int i = tid; i < (int)kSurvivorsMax + 4; i += nthreads) {
       fs.key[i] = 0u;  // padding: below every real key
       fs.idx[i] = 0x7FFFFFFF;
     }
-    if (wave == 0) {
-      const uint32_t t = wave_bound(m, n_max, k);
+    for (int i = tid; i < 256; i += nthreads) fs.hist[i] = 0u;
+    if (tid == 0) {
+      fs.count = 0u;
+      fs.n_over = 0u;
+    }
+    const uint32_t key = float_key(__uint_as_float(he.x));
+    const bool is_max = tid < n_heads && (tid % kHeads) == 0 && (int32_t)he.y >= 0;
+    {
+      const uint32_t lo = wave_min_u32(is_max ? key : 0xFFFFFFFFu);
+      const uint32_t hi = wave_max_u32(is_max ? key : 0u);
       if (lane == 0) {
-        fs.bound = t;
-        fs.count = 0u;
-        fs.n_over = 0u;
+        fs.wmin[wave] = lo;
+        fs.wmax[wave] = hi;
       }
     }
     lds_barrier();
-    const uint32_t t = fs.bound;
+    // T: the maxima share the bits above their highest differing bit; one
+    // histogram over the next 8 bits finds the digit d such that at least k
+    // maxima have digit >= d, and T = (shared bits, d, zeros) is at most the
+    // k-th largest maximum, hence at most the row's k-th largest value
+    // (those maxima are k distinct logits).
+    const int nw = nthreads >> 6;
+    const uint32_t gmin = wave_min_u32(lane < nw ? fs.wmin[lane] : 0xFFFFFFFFu);
+    const uint32_t gmax = wave_max_u32(lane < nw ? fs.wmax[lane] : 0u);
+    int shift = 0;
+    if (gmin != gmax) {
+      const int top = 31 - __clz(gmin ^ gmax);
+      shift = top >= 7 ? top - 7 : 0;
+      if (is_max) atomicAdd(&fs.hist[(key >> shift) & 0xFFu], 1u);
+    }
+    lds_barrier();
+    uint32_t t = gmin;  // all maxima equal: every one is >= T
+    if (gmin != gmax) {
+      const uint4 h = *reinterpret_cast<const uint4*>(&fs.hist[4 * lane]);
+      const uint32_t s3 = h.w, s2 = h.z + s3, s1 = h.y + s2, s0 = h.x + s1;
+      const uint32_t incl = wave_scan_inclusive(s0);
+      const uint32_t after = readlane_u32(incl, 63) - incl;  // maxima in the digits of higher lanes
+      const uint64_t have = ballot(s0 + after >= k);
+      const int L = 63 - __clzll(have);
+      const uint32_t i_star = s3 + after >= k ? 3u : s2 + after >= k ? 2u : s1 + after >= k ? 1u : 0u;
+      const uint32_t digit = 4u * (uint32_t)L + readlane_u32(i_star, L);
+      const uint32_t low = shift + 8 >= 32 ? 0xFFFFFFFFu : (1u << (shift + 8)) - 1u;
+      t = (gmax & ~low) | (digit << shift);
+    }
     const bool mine = tid < n_heads && (int32_t)he.y >= 0;
-    const uint32_t key = float_key(__uint_as_float(he.x));
     // a chunk with more candidates than heads may hold survivors beyond them
     const bool over = kc > kHeads && (int32_t)hl.y >= 0 && float_key(__uint_as_float(hl.x)) >= t;
     place_survivor(fs, mine && !over && key >= t, key, he.x, (int32_t)he.y);
     if (tid < n_heads && over && e == c * kHeads) fs.over[atomicAdd(&fs.n_over, 1u)] = c;
     lds_barrier();
-    const uint32_t n_over = fs.n_over;
+    const uint32_t n_over = uniform(fs.n_over);
     if (n_over) {  // rare: read those chunks' candidate lists in full
       const int64_t total = (int64_t)n_over * kc;
       for (int64_t base = 0; base < total; base += nthreads) {
@@ -724,7 +730,7 @@ __device__ void merge_final(const uint2* in, int64_t n_in, const uint2* heads, i
         uint2 x = make_uint2(0u, 0xFFFFFFFFu);
         uint32_t kx = 0u;
         if (j < total) {
-          x = in[(int64_t)fs.over[j / kc] * kc + j % kc];
+          x = ld_cand(&in[(int64_t)fs.over[j / kc] * kc + j % kc]);
           kx = float_key(__uint_as_float(x.x));
           take = (int32_t)x.y >= 0 && kx >= t;
         }
@@ -732,9 +738,17 @@ __device__ void merge_final(const uint2* in, int64_t n_in, const uint2* heads, i
       }
       lds_barrier();
     }
-    const uint32_t n = fs.count;
+    const uint32_t n = uniform(fs.count);
     if (n <= kSurvivorsMax) {
-      rank_and_write(fs, n, k, values, indices);
+      rank_count(fs.key, fs.idx, n, fs.rank);
+      lds_barrier();
+      for (uint32_t i = tid; i < n; i += nthreads) {
+        const uint32_t r = fs.rank[i];
+        if (r < k) {
+          values[r] = __uint_as_float(fs.bits[i]);
+          indices[r] = (int64_t)fs.idx[i];
+        }
+      }
       return;
     }
   }
@@ -747,7 +761,7 @@ __device__ void merge_final(const uint2* in, int64_t n_in, const uint2* heads, i
 #pragma unroll
   for (int r = 0; r < RM; ++r) {
     const int64_t pos = (int64_t)(wave * RM + r) * 64 + lane;
-    const uint2 x = in[pos < n_in ? pos : n_in - 1];
+    const uint2 x = ld_cand(&in[pos < n_in ? pos : n_in - 1]);
     vb[r] = x.x;
     idx[r] = (int32_t)x.y;
     key[r] = float_key(__uint_as_float(x.x));
@@ -766,6 +780,58 @@ __device__ void merge_final(const uint2* in, int64_t n_in, const uint2* heads, i
   }
   lds_barrier();
   rank_and_write(fs, n, k, values, indices);
+}
+
+// LDS of a chunk kernel: the chunk selection's staging, and, after it, the
+// final merge of the fused path.
+union ChunkSmem {
+  HeadStage hs;
+  FinalSmem fs;
+};
+
+// What the fused final merge needs: the launch's candidate lists and heads,
+// the outputs, and a workspace counter that is zero between calls.
+struct FusedMerge {
+  uint32_t* counter;
+  const uint2* cand;   // [M][n_chunks][kc]
+  const uint2* heads;  // [M][n_chunks][kHeads]
+  float* values;       // [M][k]
+  int64_t* indices;    // [M][k]
+  int M;
+  int n_chunks;
+  int kc;
+  int k;
+};
+
+// Fused second pass (lm-head-topk page, section "Method": the chunk
+// candidates are merged into the final top-k).  Called by every workgroup
+// of a chunk launch (one workgroup per chunk) after it has stored its
+// candidates and heads with st_cand.  Each workgroup waits until those
+// stores are complete at device scope, then counts itself done on the
+// counter; the workgroup that counts last sees every chunk's candidates and
+// merges all M rows, then sets the counter back to zero for the next call.
+// n_chunks * kc <= blockDim.x * RM.
+template <int RM>
+__device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem& sm, FinalSmem& fs,
+                                 uint32_t& last) {
+  // every store of this thread has been acknowledged (gfx9 counts stores in vmcnt)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  if (threadIdx.x == 0) {
+    const uint32_t done =
+        __hip_atomic_fetch_add(f.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = done == (uint32_t)f.n_chunks - 1u ? 1u : 0u;
+  }
+  lds_barrier();
+  if (uniform(last) == 0u) return;
+  const int64_t n_in = (int64_t)f.n_chunks * f.kc;
+  for (int m = 0; m < f.M; ++m) {
+    merge_final<RM>(f.cand + (size_t)m * n_in, n_in, f.heads + (size_t)m * f.n_chunks * kHeads,
+                    f.n_chunks, f.kc, (uint32_t)f.k, f.values + (size_t)m * f.k,
+                    f.indices + (size_t)m * f.k, (int)blockDim.x, sm, fs);
+    lds_barrier();  // fs is reused by the next row
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(f.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace lmtopk

@@ -9,6 +9,7 @@ namespace lmtopk {
 
 constexpr int kMaxMergeLevels = 8;
 constexpr int64_t kSegMax = 16384;  // candidates one merge workgroup can hold (1024 x 16)
+constexpr int64_t kFusedSlots = 16; // candidate slots per thread of the fused final merge
 
 struct MergeLevel {
   int64_t n_in;  // candidates per row read by this level
@@ -28,8 +29,10 @@ struct Geometry {
   int n_chunks;
   int kc;          // candidate slots per chunk per row = min(k, C)
   int64_t n_tiles; // 64-row tiles covering V
-  int n_levels;    // merge kernel launches
+  int n_levels;    // merge kernel launches (0 when fused)
+  int fused;       // the chunk launch's last workgroup does the final merge
   MergeLevel level[kMaxMergeLevels];
+  size_t sync_bytes;     // completion counter of the fused merge (zero between calls)
   size_t heads_bytes;    // best candidates of each chunk [M][n_chunks][4] x 8 B
   size_t region0_bytes;  // chunk candidates [M][n_chunks * kc] x 8 B
   size_t region1_bytes;  // first intermediate merge output, or 0
@@ -45,12 +48,13 @@ int launch_pack(const void* w, int w_is_bf16, int64_t V, int64_t H, void* wq, fl
                 void* stream);
 int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* act_scale,
                          const void* wq, const float* wscale, const float* bias, int64_t H,
-                         void* workspace, void* stream, void* const* events);
+                         void* workspace, float* values, int64_t* indices, void* stream,
+                         void* const* events);
 int launch_dense_chunks(const Geometry& g, const void* hidden, const void* weight, int is_bf16,
-                        const float* bias, int64_t H, void* workspace, void* stream,
-                        void* const* events);
+                        const float* bias, int64_t H, void* workspace, float* values,
+                        int64_t* indices, void* stream, void* const* events);
 int launch_select_chunks(const Geometry& g, const float* logits, int64_t ld, void* workspace,
-                         void* stream, void* const* events);
+                         float* values, int64_t* indices, void* stream, void* const* events);
 int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* indices,
                   void* stream);
 // Largest LDS (bytes) one workgroup may use on the current device.

@@ -44,11 +44,12 @@ def test_layout_and_sizes():
     assert lt.packed_bytes(248320, 5120) == (158924800, 39731200)   # signs + fp32 scales
     assert lt.packed_bytes(32001, 2048) == (32064 * 2048 // 8, 32064 * 16 * 4)
     assert lt.packed_bytes(1, 640) == (64 * 640 // 8, 64 * 8 * 4)   # G=5 pads to 8 scales
-    # chunk heads (243 x 4 x 8 B rounded to 256) + chunk candidates of the flagship
-    # (243 chunks x 50 x 8 B rounded to 256); one workgroup merges them, no second region
-    assert lt.workspace_bytes(1, 248320, 50) == 7936 + 97280
+    # completion counter (256 B) + chunk heads (243 x 4 x 8 B rounded to 256) + chunk
+    # candidates of the flagship (243 chunks x 50 x 8 B rounded to 256); one workgroup
+    # merges them, no second region
+    assert lt.workspace_bytes(1, 248320, 50) == 256 + 7936 + 97280
     # k >= chunk rows: every chunk offers all its rows, and the merge needs two levels
-    assert lt.workspace_bytes(8, 248320, 1024) == (8 * 243 * 32 + 8 * 243 * 1024 * 8
+    assert lt.workspace_bytes(8, 248320, 1024) == (256 + 8 * 243 * 32 + 8 * 243 * 1024 * 8
                                                    + 8 * 16 * 1024 * 8)
 
 

@@ -212,3 +212,20 @@ def test_small_k_chunk_path_ragged_tails(V, k):
     assert_select_exact(x, v, i, k)
     v2, i2 = run_select(x, k, 2048)
     assert np.array_equal(i, i2)
+
+
+def test_fused_merge_counter_is_left_zero_and_workspace_is_shared():
+    # A call whose candidates fit one chunk workgroup merges in the last
+    # workgroup to finish, counted on the workspace's first word, which every
+    # call leaves at zero.  One workspace serves fused (k = 50, 7) and
+    # two-level (k = 1024) calls in any order, and repeated calls.
+    V = 248320
+    x = synthetic.random_logits(8, V, seed=77, ties=100)
+    t = dev(x)
+    ws = lt.new_workspace(8, V, 1024, device="cuda")
+    assert lt.workspace_bytes(8, V, 50) <= ws.numel()
+    for k in (50, 1024, 7, 50, 1024, 50):
+        v, i = lt.topk_logits(t, k, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:256].count_nonzero()) == 0, f"completion counter not reset after k={k}"
+        assert_select_exact(x, v.cpu().numpy(), i.cpu().numpy(), k)
