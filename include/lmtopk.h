@@ -118,8 +118,8 @@ typedef struct {
 #define LMTOPK_GROUP_SIZE 128
 #define LMTOPK_MAX_ROWS 8
 #define LMTOPK_MAX_K 2048
-/* Binary path: the activation trit masks of all M rows live in LDS
-   (196 bytes per row and group of 128, about 1.5 * M * H bytes). */
+/* Binary path: the activation bit planes of all M rows live in LDS
+   (132 bytes per row and group of 128, about 1.03 * M * H bytes). */
 #define LMTOPK_MAX_BINARY_MH 65536
 
 /* Layout version of packed heads this library reads and writes. */

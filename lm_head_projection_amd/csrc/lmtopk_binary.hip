@@ -13,19 +13,20 @@ namespace lmtopk {
 
 constexpr int kGroup = 128;
 
-// Activations in balanced ternary.  Every int8 activation a is written as
-// a = sum_{p<6} 3^p d_p with digits d_p in {-1, 0, +1} (six trits reach
-// +-364).  For one group of 128 activations and trit p, two bit masks are
-// kept: NZ_p (d_p != 0) and POS_p (d_p == +1).  With the sign bits b of one
-// weight row (bit 1 = +1) the group's trit-p dot is
-//   sum_j sign_j d_pj = 2 popcount(XNOR(b, POS_p) AND NZ_p) - popcount(NZ_p),
-// so the exact integer group dot is
-//   D = sum_j a_j sign_j = 2 S - C,   S = sum_p 3^p popcount(XNOR(b, POS_p) AND NZ_p),
-//   C = sum_p 3^p popcount(NZ_p)  (the same for every weight row).
-// Per 32 weights and trit that is one 3-input bit operation (v_bitop3) and
-// one accumulating popcount (v_bcnt), 48 + 5 Horner steps per group of 128.
-struct TritGroup {
-  uint4 pos_nz[12];  // [trit p] -> {POS_p, NZ_p}, 4 words = 128 activations each
+// Activations as two's-complement bit planes.  Every int8 activation is
+// a = sum_{p<8} c_p a_p with bits a_p and weights c_p = 2^p (p < 7),
+// c_7 = -128.  For one group of 128 activations and bit p the plane P_p
+// holds a_p of each activation (4 words, bit b of word w = activation
+// 32 w + b).  With the sign bits b of one weight row (bit 1 = +1, so
+// sign_j = 2 b_j - 1) the exact integer group dot is
+//   D = sum_j a_j sign_j = 2 S - C,
+//   S = sum_j a_j b_j = sum_p c_p sum_{w<4} popcount(b_w AND P_pw),
+//   C = sum_j a_j  (the same for every weight row).
+// S is accumulated by Horner's rule over the planes, top plane first.  Per
+// 32 weights and plane that is one AND and one accumulating popcount
+// (v_bcnt): 64 operations and 8 mask reads of 16 bytes per group of 128.
+struct PlaneGroup {
+  uint4 plane[8];  // [bit p] -> P_p, 4 words = 128 activations
 };
 
 struct BinaryArgs {
@@ -50,24 +51,23 @@ __device__ __forceinline__ float comp4(const float4& f, int i) {
   return i == 0 ? f.x : i == 1 ? f.y : i == 2 ? f.z : f.w;
 }
 
-// S of one group for R weight rows at once: the trit masks are read once and
-// serve all R rows.
+// S of one group for R weight rows at once: each plane is read once and
+// serves all R rows.
 template <int R>
-__device__ __forceinline__ void trit_dot(const uint4 (&w)[R], const uint4* tg, uint32_t (&u)[R]) {
+__device__ __forceinline__ void plane_dot(const uint4 (&w)[R], const uint4* pg, uint32_t (&u)[R]) {
 #pragma unroll
   for (int r = 0; r < R; ++r) u[r] = 0u;
 #pragma unroll
-  for (int p = 5; p >= 0; --p) {
-    const uint4 pos = tg[2 * p];
-    const uint4 nz = tg[2 * p + 1];
+  for (int p = 7; p >= 0; --p) {
+    const uint4 pl = pg[p];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      uint32_t x = (u[r] << 1) + u[r];
-      x = bcnt_acc(~(w[r].x ^ pos.x) & nz.x, x);
-      x = bcnt_acc(~(w[r].y ^ pos.y) & nz.y, x);
-      x = bcnt_acc(~(w[r].z ^ pos.z) & nz.z, x);
-      x = bcnt_acc(~(w[r].w ^ pos.w) & nz.w, x);
-      u[r] = x;
+      uint32_t x = bcnt_acc(w[r].x & pl.x, 0u);
+      x = bcnt_acc(w[r].y & pl.y, x);
+      x = bcnt_acc(w[r].z & pl.z, x);
+      x = bcnt_acc(w[r].w & pl.w, x);
+      // S = (...((-S_7) * 2 + S_6) * 2 + ...) + S_0, in two's complement
+      u[r] = p == 7 ? 0u - x : (u[r] << 1) + x;
     }
   }
 }
@@ -79,7 +79,7 @@ __device__ __forceinline__ void trit_dot(const uint4 (&w)[R], const uint4* tg, u
 // every row takes the same operation sequence wherever it sits.
 //
 // Latency: the activation bytes are requested first and the first two quads
-// of weights right after them; the trit masks are built while those weights
+// of weights right after them; the bit planes are built while those weights
 // are in flight (the barriers here only order LDS, so they do not wait for
 // the weight loads).  In the steady state two quads are in flight while one
 // is computed; the loads are issued unconditionally and pinned in place so
@@ -99,9 +99,8 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   HeadStage& hst = csm.hs;
   for (int i = threadIdx.x; i < kMaxK; i += blockDim.x) hst.rank[i] = 0u;  // ordered by the barriers below
   const int G = a.G;
-  uint16_t* table = reinterpret_cast<uint16_t*>(dyn_lds);             // [256] trit codes
-  TritGroup* tgs = reinterpret_cast<TritGroup*>(dyn_lds + 512);       // [M][G]
-  int* cg = reinterpret_cast<int*>(tgs + (size_t)M * G);              // [M][G] C of the group
+  PlaneGroup* pgs = reinterpret_cast<PlaneGroup*>(dyn_lds);          // [M][G]
+  int* cg = reinterpret_cast<int*>(pgs + (size_t)M * G);              // [M][G] C of the group
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
@@ -123,25 +122,8 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   // Prologue.  Everything whose load count depends on the shapes happens
   // before the weight prefetch, and the prefetch is followed only by
   // straight-line code, so the waits after it cover exactly what they need.
-  // 1. trit code of every int8 value: bits 0..5 NZ_p, bits 8..13 POS_p
-  for (int e = tid; e < 256; e += blockDim.x) {
-    int v = e < 128 ? e : e - 256;
-    uint32_t c = 0u;
-#pragma unroll
-    for (int p = 0; p < 6; ++p) {
-      int r = v % 3;  // in {-2, ..., 2}
-      if (r == 2) r = -1;
-      if (r == -2) r = 1;
-      if (r != 0) c |= 1u << p;
-      if (r == 1) c |= 1u << (8 + p);
-      v = (v - r) / 3;
-    }
-    table[e] = (uint16_t)c;
-  }
-  lds_barrier();
-
-  // 2. trit masks of a batch of groups: each mask word is one ballot over 64
-  //    activations (groups b0, b0 + nw, ..., this wave's share)
+  // 1. bit planes of a batch of groups: each plane word is one ballot over
+  //    64 activations (groups b0, b0 + nw, ..., this wave's share)
   constexpr int kBatch = 4;
   const int n_mg = M * G;
   auto load_acts = [&](int b0, int8_t (&y0)[kBatch], int8_t (&y1)[kBatch]) {
@@ -160,22 +142,17 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     for (int i = 0; i < kBatch; ++i) {
       const int mg = b0 + i * nw;
       if (mg >= n_mg) break;
-      const uint32_t c0 = table[(uint8_t)y0[i]];
-      const uint32_t c1 = table[(uint8_t)y1[i]];
+      const uint32_t a0 = (uint8_t)y0[i], a1 = (uint8_t)y1[i];
       uint4 mine = make_uint4(0u, 0u, 0u, 0u);
-      int cgroup = 0, w3 = 1;
+      int cgroup = 0;
 #pragma unroll
-      for (int p = 0; p < 6; ++p) {
-        const uint64_t p0 = ballot((c0 >> (8 + p)) & 1u), p1 = ballot((c1 >> (8 + p)) & 1u);
-        const uint64_t n0 = ballot((c0 >> p) & 1u), n1 = ballot((c1 >> p) & 1u);
-        if (lane == 2 * p)
-          mine = make_uint4((uint32_t)p0, (uint32_t)(p0 >> 32), (uint32_t)p1, (uint32_t)(p1 >> 32));
-        if (lane == 2 * p + 1)
-          mine = make_uint4((uint32_t)n0, (uint32_t)(n0 >> 32), (uint32_t)n1, (uint32_t)(n1 >> 32));
-        cgroup += w3 * (__popcll(n0) + __popcll(n1));
-        w3 *= 3;
+      for (int p = 0; p < 8; ++p) {
+        const uint64_t b0 = ballot((a0 >> p) & 1u), b1 = ballot((a1 >> p) & 1u);
+        if (lane == p)
+          mine = make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1, (uint32_t)(b1 >> 32));
+        cgroup += (p == 7 ? -128 : 1 << p) * (__popcll(b0) + __popcll(b1));
       }
-      if (lane < 12) tgs[mg].pos_nz[lane] = mine;
+      if (lane < 8) pgs[mg].plane[lane] = mine;
       if (lane == 0) cg[mg] = cgroup;
     }
   };
@@ -245,7 +222,7 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       uint32_t u[R];
-      trit_dot<R>(w, tgs[(size_t)m * G + g].pos_nz, u);
+      plane_dot<R>(w, pgs[(size_t)m * G + g].plane, u);
       const int c = cg[m * G + g];
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[r][m] = fmaf((float)(2 * (int)u[r] - c), s[r], acc[r][m]);
@@ -363,7 +340,7 @@ void (*binary_kernel(int M, int rpl))(BinaryArgs) {
 
 size_t binary_lds_bytes(int64_t M, int64_t H) {
   const int64_t G = H / kGroup;
-  return (size_t)(512 + M * G * sizeof(TritGroup) + M * G * 4);
+  return (size_t)(M * G * sizeof(PlaneGroup) + M * G * 4);
 }
 int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* act_scale,
                          const void* wq, const float* wscale, const float* bias, int64_t H,
