@@ -179,9 +179,10 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
       bias_v[r] = bp[v];
     }
   }
-  float act_s[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) act_s[m] = a.act_scale[m];
+  // row scales: lane m holds row m's (a per-lane load: a scalar load would
+  // hold up the barrier below, which waits for every scalar load, by a full
+  // memory round trip)
+  const float act_sv = a.act_scale[lane < M ? lane : M - 1];
   __builtin_amdgcn_sched_barrier(0);
   // every wave's activation requests go out before any wave's weight
   // requests: the CU serves its requests in order, so otherwise the last
@@ -304,13 +305,13 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   }
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const float s = act_s[m];
+    const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(act_sv), m));
     float val[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) val[r] = fmaf(acc[r][m], s, bias_v[r]);
     chunk_select_write<R>(val, idx, valid, m, a.out, ssm, hst, m == M - 1);
   }
-  if (a.out.fused) fused_merge_tail<kFusedRM>(a.out.merge, ssm, csm.fs, last_wg);
+  if (a.out.fused) fused_merge_tail<kFusedRM>(fused_merge_of(a.out), ssm, csm.fs, last_wg);
 }
 namespace {
 

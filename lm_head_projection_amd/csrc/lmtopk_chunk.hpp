@@ -14,14 +14,32 @@
 namespace lmtopk {
 
 struct ChunkOut {
-  uint2* cand;   // [M][n_chunks][kc]
-  uint2* heads;  // [M][n_chunks][kHeads]
+  uint2* cand;        // [M][n_chunks][kc]
+  uint2* heads;       // [M][n_chunks][kHeads]
+  uint32_t* counter;  // completion counter of the fused merge
+  float* values;      // [M][k] final outputs (fused merge)
+  int64_t* indices;   // [M][k]
   int n_chunks;
   int kc;
   int k;
-  int fused;     // the launch's last workgroup merges (fused_merge_tail)
-  FusedMerge merge;
+  int M;
+  int fused;          // the launch's last workgroup merges (fused_merge_tail)
 };
+
+// The fused merge's view of a chunk launch's outputs.
+__device__ __forceinline__ FusedMerge fused_merge_of(const ChunkOut& o) {
+  FusedMerge f;
+  f.counter = o.counter;
+  f.cand = o.cand;
+  f.heads = o.heads;
+  f.values = o.values;
+  f.indices = o.indices;
+  f.M = o.M;
+  f.n_chunks = o.n_chunks;
+  f.kc = o.kc;
+  f.k = o.k;
+  return f;
+}
 
 // Candidate slots per thread of the fused final merge (n_chunks * kc <=
 // 16 * threads per chunk workgroup; the host checks it).
@@ -118,15 +136,10 @@ inline ChunkOut chunk_out(const Geometry& g, void* workspace, float* values, int
   o.kc = g.kc;
   o.k = g.k;
   o.fused = g.fused;
-  o.merge.counter = reinterpret_cast<uint32_t*>(ws);
-  o.merge.cand = o.cand;
-  o.merge.heads = o.heads;
-  o.merge.values = values;
-  o.merge.indices = indices;
-  o.merge.M = (int)g.M;
-  o.merge.n_chunks = g.n_chunks;
-  o.merge.kc = g.kc;
-  o.merge.k = g.k;
+  o.counter = reinterpret_cast<uint32_t*>(ws);
+  o.values = values;
+  o.indices = indices;
+  o.M = (int)g.M;
   return o;
 }
 }  // namespace lmtopk

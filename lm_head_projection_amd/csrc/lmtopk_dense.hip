@@ -117,7 +117,7 @@ __global__ __launch_bounds__(1024) void k_dense_chunk(DenseArgs a) {
     for (int r = 0; r < RPL; ++r) val[r] = ((valid >> r) & 1u) ? scores[m * C + lr[r]] : 0.f;
     chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm, hst, m == M - 1);
   }
-  if (a.out.fused) fused_merge_tail<kFusedRM>(a.out.merge, ssm, csm.fs, last_wg);
+  if (a.out.fused) fused_merge_tail<kFusedRM>(fused_merge_of(a.out), ssm, csm.fs, last_wg);
 }
 namespace {
 
