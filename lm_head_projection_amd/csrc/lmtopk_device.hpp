@@ -340,7 +340,7 @@ constexpr uint32_t kSmallSurvivorsMax = 256;
 // the small-k path's per-wave tops.
 struct alignas(16) HeadStage {
   uint32_t tops[kMaxWaves * kWaveTops];
-  uint32_t trank[kMaxWaves * kWaveTops];  // ranks of the tops, zero between uses
+  uint32_t trank[kMaxWaves * kWaveTops];  // per top: the tops >= it; zero between uses
   uint32_t hkey[kMaxWaves * kHeads];  // block_heads: each wave's best entries
   int32_t hidx[kMaxWaves * kHeads];
   uint32_t hbits[kMaxWaves * kHeads];
@@ -353,14 +353,21 @@ struct alignas(16) HeadStage {
   uint32_t count;
 };
 
-// rank[i] += the number of entries ahead of entry i among n entries in LDS:
-// greater key, or equal key and lower idx (idx == nullptr: lower position).
-// The work is spread over every wave of the workgroup: job (slice s, block
-// b) compares the 64 entries of block b with the four entries of slice s,
-// read as one LDS broadcast, and adds the counts with one LDS atomic per
-// entry (integer adds, so the result does not depend on their order).  key
-// and idx must be readable up to index 4 * ceil(n / 4); rank[0, n) must be
-// zero on entry; the caller orders the result with a barrier.
+// Counting over n entries in LDS, for each entry i < n:
+//   kAhead: rank[i] += #{j : key[j] > key[i], or key[j] == key[i] and
+//           idx[j] < idx[i]} (idx == nullptr: positions instead of idx), the
+//           entry's position in (key desc, idx asc) order;
+//   else:   rank[i] += #{j : key[j] >= key[i]} (idx unused; the entry itself
+//           counts).
+// Wave w takes the slices of 16 entries j = w, w + nw, ... (each read as
+// four LDS broadcasts per array) against every block of 64 entries i, and
+// adds a slice's count with one LDS atomic per entry (integer adds: the
+// result does not depend on their order).  Few wide slices keep the
+// per-slice overhead small; the whole workgroup's VALU is one shared pool.
+// key and idx must be readable up to index 16 * ceil(n / 16) (entries past
+// n are not counted); rank[0, n) must be zero on entry; the caller orders
+// the result with a barrier.
+template <bool kAhead = true>
 __device__ __forceinline__ void rank_count(const uint32_t* key, const int32_t* idx, uint32_t n,
                                            uint32_t* rank) {
   n = uniform(n);
@@ -368,24 +375,42 @@ __device__ __forceinline__ void rank_count(const uint32_t* key, const int32_t* i
   const int lane = lane_id();
   const uint32_t wave = (uint32_t)wave_id(), nw = blockDim.x >> 6;
   const uint32_t nb = (n + 63u) >> 6;
-  const uint32_t ns = (n + 3u) >> 2;
-  for (uint32_t job = wave; job < ns * nb; job += nw) {
-    const uint32_t sl = job % ns, b = job / ns;
-    const uint32_t j0 = sl * 4u;
-    const uint32_t i = b * 64u + (uint32_t)lane;
-    const bool vi = i < n;
-    const uint32_t ki = vi ? key[i] : 0u;
-    const int32_t ii = vi ? (idx ? idx[i] : (int32_t)i) : 0;
-    const uint4 kq = *reinterpret_cast<const uint4*>(&key[j0]);
-    const int4 iq = idx ? *reinterpret_cast<const int4*>(&idx[j0])
-                        : make_int4((int)j0, (int)j0 + 1, (int)j0 + 2, (int)j0 + 3);
-    const uint32_t kj[4] = {kq.x, kq.y, kq.z, kq.w};
-    const int32_t ij[4] = {iq.x, iq.y, iq.z, iq.w};
-    uint32_t c = 0u;
+  const uint32_t ns = (n + 15u) >> 4;
+  for (uint32_t sl = wave; sl < ns; sl += nw) {
+    const uint32_t j0 = sl * 16u;
+    uint32_t kj[16];
+    int32_t ij[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      c += (j0 + e < n && (kj[e] > ki || (kj[e] == ki && ij[e] < ii))) ? 1u : 0u;
-    if (vi && c) atomicAdd(&rank[i], c);
+    for (int q = 0; q < 4; ++q) {
+      const uint4 kq = *reinterpret_cast<const uint4*>(&key[j0 + 4 * q]);
+      kj[4 * q] = kq.x;
+      kj[4 * q + 1] = kq.y;
+      kj[4 * q + 2] = kq.z;
+      kj[4 * q + 3] = kq.w;
+      if (kAhead) {
+        const int4 iq = idx ? *reinterpret_cast<const int4*>(&idx[j0 + 4 * q])
+                            : make_int4((int)j0 + 4 * q, (int)j0 + 4 * q + 1, (int)j0 + 4 * q + 2,
+                                        (int)j0 + 4 * q + 3);
+        ij[4 * q] = iq.x;
+        ij[4 * q + 1] = iq.y;
+        ij[4 * q + 2] = iq.z;
+        ij[4 * q + 3] = iq.w;
+      }
+    }
+    const uint32_t m = min(16u, n - j0);  // real entries in this slice
+    for (uint32_t b = 0; b < nb; ++b) {
+      const uint32_t i = b * 64u + (uint32_t)lane;
+      const bool vi = i < n;
+      const uint32_t ki = vi ? key[i] : 0u;
+      const int32_t ii = (kAhead && vi) ? (idx ? idx[i] : (int32_t)i) : 0;
+      uint32_t c = 0u;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const bool hit = kAhead ? (kj[e] > ki || (kj[e] == ki && ij[e] < ii)) : kj[e] >= ki;
+        c += ((uint32_t)e < m && hit) ? 1u : 0u;
+      }
+      if (vi && c) atomicAdd(&rank[i], c);
+    }
   }
 }
 
@@ -508,14 +533,14 @@ __device__ uint32_t select_top_small(const uint32_t (&key)[R], uint32_t valid,
   const int E = nw * kWaveTops;  // <= 64
   const uint32_t c = lane < nw ? st.wvalid[lane] : 0u;
   const uint32_t total = readlane_u32(row_scan_inclusive(c), 15);
-  if (total > k) rank_count(st.tops, nullptr, (uint32_t)E, st.trank);
+  if (total > k) rank_count<false>(st.tops, nullptr, (uint32_t)E, st.trank);
   lds_barrier();
 
   // 3. stage the rows with key >= T (one atomic per wave reserves its slots)
   uint32_t t = 1u;  // keeps every valid row (real keys are never 0)
   if (total > k) {
-    const uint64_t at = ballot(lane < E && st.trank[lane] == k - 1u);
-    const uint32_t b = readlane_u32(lane < E ? st.tops[lane] : 0u, at ? __ffsll((long long)at) - 1 : 0);
+    // the largest top with at least k tops >= it is the k-th largest
+    const uint32_t b = wave_max_u32(lane < E && st.trank[lane] >= k ? st.tops[lane] : 0u);
     if (b != 0u) t = b;  // else fewer than k real tops: keep every valid row
   }
   uint64_t sv[R];
