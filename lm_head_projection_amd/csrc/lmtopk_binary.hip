@@ -97,7 +97,7 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   __shared__ ChunkSmem csm;
   __shared__ uint32_t last_wg;
   HeadStage& hst = csm.hs;
-  for (int i = threadIdx.x; i < kMaxK; i += blockDim.x) hst.rank[i] = 0u;  // ordered by the barriers below
+  head_stage_init(hst);  // ordered by the barriers below
   const int G = a.G;
   PlaneGroup* pgs = reinterpret_cast<PlaneGroup*>(dyn_lds);          // [M][G]
   int* cg = reinterpret_cast<int*>(pgs + (size_t)M * G);              // [M][G] C of the group

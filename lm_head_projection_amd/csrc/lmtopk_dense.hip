@@ -51,7 +51,7 @@ __global__ __launch_bounds__(1024) void k_dense_chunk(DenseArgs a) {
   __shared__ ChunkSmem csm;
   __shared__ uint32_t last_wg;
   HeadStage& hst = csm.hs;
-  for (int i = threadIdx.x; i < kMaxK; i += blockDim.x) hst.rank[i] = 0u;  // ordered by the barriers below
+  head_stage_init(hst);  // ordered by the barriers below
   float* scores = reinterpret_cast<float*>(dyn_lds);  // [M][C]
   const int C = a.chunk_rows;
   const int tid = threadIdx.x;

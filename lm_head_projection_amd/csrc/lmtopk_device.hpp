@@ -339,19 +339,31 @@ constexpr uint32_t kSmallSurvivorsMax = 256;
 // LDS of the chunk selection's second stage: staged entries, their ranks and
 // the small-k path's per-wave tops.
 struct alignas(16) HeadStage {
-  uint32_t tops[kMaxWaves * kWaveTops];
-  uint32_t trank[kMaxWaves * kWaveTops];  // per top: the tops >= it; zero between uses
-  uint32_t hkey[kMaxWaves * kHeads];  // block_heads: each wave's best entries
+  uint32_t tops[kMaxWaves * kWaveTops];  // select_top_small: the providers' tops
+  uint32_t hkey[kMaxWaves * kHeads];     // block_heads: each wave's best entries
   int32_t hidx[kMaxWaves * kHeads];
   uint32_t hbits[kMaxWaves * kHeads];
   uint32_t key[kMaxK];
   uint32_t bits[kMaxK];
   int32_t idx[kMaxK];
   uint32_t rank[kMaxK];  // zero between uses
-  uint32_t wvalid[kMaxWaves];
-  uint32_t thr;
-  uint32_t count;
+  // select_top_small's scalars, zero between uses
+  uint32_t count;      // staged rows
+  uint32_t tops_done;  // provider waves that have published their tops
+  uint32_t thr_ready;  // thr is valid
+  uint32_t thr;        // T
 };
+
+// Puts st in the state select_top_small and block_heads expect on entry;
+// the caller orders it before their first use with a barrier.
+__device__ __forceinline__ void head_stage_init(HeadStage& st) {
+  for (int i = threadIdx.x; i < kMaxK; i += blockDim.x) st.rank[i] = 0u;
+  if (threadIdx.x == 0) {
+    st.count = 0u;
+    st.tops_done = 0u;
+    st.thr_ready = 0u;
+  }
+}
 
 // Counting over n entries in LDS, for each entry i < n:
 //   kAhead: rank[i] += #{j : key[j] > key[i], or key[j] == key[i] and
@@ -480,18 +492,32 @@ __device__ void block_heads(const uint32_t (&key)[R], uint32_t valid, const uint
   }
 }
 
+// T in the LDS address space: volatile accesses through a generic pointer
+// would become flat accesses, which wait for every outstanding global load.
+template <typename T>
+using lds_t = __attribute__((address_space(3))) T;
+
+// Bound of a wave's wait for the selection threshold (polls with a short
+// sleep each; the wave that publishes it never waits for anything).
+constexpr int kThresholdSpinMax = 1 << 22;
+
 // Exact top-k of one chunk row for small k (k <= kWaveTops * waves), without
-// radix passes.  Each wave takes its kWaveTops largest keys; the k-th largest
-// of these tops, T, is at most the chunk's k-th largest key (the tops are
-// real entries of the chunk), so every winner has key >= T.  The rows with
-// key >= T (typically a few more than k) are staged and ranked, and
-// out(pos, value_bits, index) is called for output positions pos <
-// min(k, valid rows), in no particular order of calls.  Returns that count,
-// or 0xFFFFFFFF (after writing nothing) when more than kSmallSurvivorsMax
-// rows pass T, e.g. with many equal keys.  Slot r of lane l in wave w is
-// position (w * R + r) * 64 + l as in block_select.  st.rank must be zero on
-// entry and is zero again on return.  Four barriers: after the tops, after
-// their ranks, after the staging, after the ranks of the staged rows.
+// radix passes.  The first P = 3/4 of the waves (the "providers") each take
+// their h = ceil(k / P) largest keys (P * h <= 64; else P = all waves); the
+// provider that completes this set finds T, the k-th largest of the P * h
+// tops, alone and publishes it.  T is at most the chunk's k-th largest key
+// (the tops are real entries of the chunk), so every winner has key >= T.
+// Every wave stages its rows with key >= T as soon as T is published: the
+// waves a CU serves first have finished streaming long before the last
+// ones, so T and most of the staging are ready when the last wave arrives,
+// and no barrier precedes the staging.  The staged rows (typically a few
+// more than k) are ranked after one barrier, and out(pos, value_bits,
+// index) is called for output positions pos < min(k, valid rows), in no
+// particular order of calls.  Returns that count, or 0xFFFFFFFF (after
+// writing nothing) when more than kSmallSurvivorsMax rows pass T, e.g. with
+// many equal keys.  Slot r of lane l in wave w is position (w * R + r) * 64
+// + l as in block_select.  st must be as head_stage_init leaves it and is so
+// again on return.  Two barriers: after the staging, after the ranks.
 template <int R, typename Out>
 __device__ uint32_t select_top_small(const uint32_t (&key)[R], uint32_t valid,
                                      const uint32_t (&vbits)[R], const int32_t (&index)[R],
@@ -500,47 +526,72 @@ __device__ uint32_t select_top_small(const uint32_t (&key)[R], uint32_t valid,
   const int lane = lane_id();
   const int wave = wave_id();
   const int nw = blockDim.x >> 6;
-
-  // 1. this wave's kWaveTops largest keys (repeats count), 0 where absent
-  uint32_t left = valid, top = 0u, nvalid = 0u;
-#pragma unroll
-  for (int r = 0; r < R; ++r) nvalid += (uint32_t)__popcll(ballot((valid >> r) & 1u));
-#pragma unroll
-  for (int h = 0; h < kWaveTops; ++h) {
-    uint32_t best = 0u;
-    int br = 0;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (((left >> r) & 1u) && key[r] > best) {
-        best = key[r];
-        br = r;
-      }
-    }
-    const uint32_t wm = wave_max_u32(best);
-    if (lane == h) top = wm;
-    if (wm == 0u) break;
-    const uint64_t holders = ballot(best == wm);
-    if (lane == __ffsll((long long)holders) - 1) left &= ~(1u << br);
+  int P = max(1, (3 * nw) / 4);
+  int h = ((int)k + P - 1) / P;
+  if (P * h > kMaxWaves * kWaveTops) {
+    P = nw;
+    h = ((int)k + nw - 1) / nw;  // <= kWaveTops
   }
-  if (lane < kWaveTops) st.tops[wave * kWaveTops + lane] = top;
-  if (lane == 0) st.wvalid[wave] = nvalid;
-  if (tid == 0) st.count = 0u;
-  for (int i = tid; i < kMaxWaves * kWaveTops; i += (int)blockDim.x) st.trank[i] = 0u;
-  lds_barrier();
+  P = uniform(P);
+  h = uniform(h);
 
-  // 2. T = the k-th largest top (ties broken by position), when more than k
-  //    rows are valid
-  const int E = nw * kWaveTops;  // <= 64
-  const uint32_t c = lane < nw ? st.wvalid[lane] : 0u;
-  const uint32_t total = readlane_u32(row_scan_inclusive(c), 15);
-  if (total > k) rank_count<false>(st.tops, nullptr, (uint32_t)E, st.trank);
-  lds_barrier();
+  // 1. providers: this wave's h largest keys (repeats count), 0 where absent
+  if (wave < P) {
+    uint32_t left = valid, top = 0u;
+    for (int j = 0; j < h; ++j) {
+      uint32_t best = 0u;
+      int br = 0;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (((left >> r) & 1u) && key[r] > best) {
+          best = key[r];
+          br = r;
+        }
+      }
+      const uint32_t wm = wave_max_u32(best);
+      if (lane == j) top = wm;
+      if (wm == 0u) break;
+      const uint64_t holders = ballot(best == wm);
+      if (lane == __ffsll((long long)holders) - 1) left &= ~(1u << br);
+    }
+    if (lane < h) st.tops[wave * h + lane] = top;
+    // the tops are written before the count (LDS operations of a wave
+    // complete in order; the fence keeps the compiler from reordering)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    uint32_t done = 0u;
+    if (lane == 0) done = atomicAdd(&st.tops_done, 1u);
+    done = readlane_u32(done, 0);
+    if (done == (uint32_t)P - 1u) {
+      // the last provider: T = the largest top with at least k tops >= it
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      const int E = P * h;  // <= 64
+      const uint32_t mine = lane < E ? st.tops[lane] : 0u;
+      uint32_t cnt = 0u;
+      for (int j0 = 0; j0 < E; j0 += 4) {
+        const uint4 q = *reinterpret_cast<const uint4*>(&st.tops[j0]);
+        cnt += (q.x >= mine ? 1u : 0u) + (j0 + 1 < E && q.y >= mine ? 1u : 0u) +
+               (j0 + 2 < E && q.z >= mine ? 1u : 0u) + (j0 + 3 < E && q.w >= mine ? 1u : 0u);
+      }
+      const uint32_t T = wave_max_u32(lane < E && cnt >= k ? mine : 0u);
+      if (lane == 0) st.thr = T;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      if (lane == 0) *(volatile lds_t<uint32_t>*)&st.thr_ready = 1u;
+    }
+  }
 
-  // 3. stage the rows with key >= T (one atomic per wave reserves its slots)
+  // 2. wait for T (bounded; on a time-out every valid row is staged, a
+  //    superset of the winners), then stage the rows with key >= T (one
+  //    atomic per wave reserves its slots)
+  uint32_t ready = 0u;
+  for (int spin = 0; spin < kThresholdSpinMax; ++spin) {
+    ready = uniform(*(volatile lds_t<uint32_t>*)&st.thr_ready);
+    if (ready) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   uint32_t t = 1u;  // keeps every valid row (real keys are never 0)
-  if (total > k) {
-    // the largest top with at least k tops >= it is the k-th largest
-    const uint32_t b = wave_max_u32(lane < E && st.trank[lane] >= k ? st.tops[lane] : 0u);
+  if (ready) {
+    const uint32_t b = uniform(*(volatile lds_t<uint32_t>*)&st.thr);
     if (b != 0u) t = b;  // else fewer than k real tops: keep every valid row
   }
   uint64_t sv[R];
@@ -567,15 +618,28 @@ __device__ uint32_t select_top_small(const uint32_t (&key)[R], uint32_t valid,
   }
   lds_barrier();
   const uint32_t n = uniform(st.count);
-  if (n > kSmallSurvivorsMax) return 0xFFFFFFFFu;
+  if (n > kSmallSurvivorsMax) {
+    lds_barrier();  // every wave has read the count
+    if (tid == 0) {
+      st.count = 0u;
+      st.tops_done = 0u;
+      st.thr_ready = 0u;
+    }
+    return 0xFFFFFFFFu;
+  }
 
-  // 4. rank the staged rows and emit the first k
+  // 3. rank the staged rows and emit the first k
   rank_count(st.key, st.idx, n, st.rank);
   lds_barrier();
   for (uint32_t i = tid; i < n; i += blockDim.x) {
     const uint32_t r = st.rank[i];
     if (r < k) out(r, st.bits[i], st.idx[i]);
     st.rank[i] = 0u;
+  }
+  if (tid == 0) {  // every wave has read them before the barrier above
+    st.count = 0u;
+    st.tops_done = 0u;
+    st.thr_ready = 0u;
   }
   return n < k ? n : k;
 }

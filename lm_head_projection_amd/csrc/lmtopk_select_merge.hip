@@ -98,7 +98,8 @@ __global__ __launch_bounds__(1024) void k_select_chunk(SelectArgs a) {
   __shared__ ChunkSmem csm;
   __shared__ uint32_t last_wg;
   HeadStage& hst = csm.hs;
-  for (int i = threadIdx.x; i < kMaxK; i += blockDim.x) hst.rank[i] = 0u;  // ordered by the selection's barriers
+  head_stage_init(hst);
+  lds_barrier();  // the selection writes LDS before its first barrier
   const int wave = wave_id();
   const int lane = lane_id();
   const int64_t base = (int64_t)blockIdx.x * a.chunk_rows;
