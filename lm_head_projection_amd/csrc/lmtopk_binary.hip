@@ -184,11 +184,8 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   // memory round trip)
   const float act_sv = a.act_scale[lane < M ? lane : M - 1];
   __builtin_amdgcn_sched_barrier(0);
-  // every wave's activation requests go out before any wave's weight
-  // requests: the CU serves its requests in order, so otherwise the last
-  // waves would wait for most of the weight prefetch before they could build
-  // their masks
-  lds_barrier();
+  // (no barrier here: each wave requests its weights as soon as it has
+  // requested its activation bytes, so HBM is busy from the first waves on)
 
   // 4. first quads of weights (group and quad indices clamped into the head),
   //    issued in the same order as the main loop's refills
