@@ -72,6 +72,23 @@ __device__ __forceinline__ void plane_dot(const uint4 (&w)[R], const uint4* pg, 
   }
 }
 
+// From four rows on (one row per lane): the sign bits of two words (64
+// elements) as 16 words of four 0/1 bytes, e[k] holding the bits of
+// elements 4k .. 4k + 3 of that half.  A nibble n is spread to the low bits
+// of four bytes by n * 0x204081 = n + (n << 7) + (n << 14) + (n << 21): the
+// four partial products occupy disjoint bits, and bit j of n lands on bit
+// 8j, the only bits the mask keeps.  The words are shared by all M rows; S
+// of a row is then one v_dot4_i32_i8 per four elements with the row's
+// activation bytes, the same exact integer as the plane sum, for 96 + 32 M
+// instructions per group against 64 M.
+__device__ __forceinline__ void spread_signs(uint32_t w0, uint32_t w1, uint32_t (&e)[16]) {
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    e[n] = (__builtin_amdgcn_ubfe(w0, 4 * n, 4) * 0x00204081u) & 0x01010101u;
+    e[8 + n] = (__builtin_amdgcn_ubfe(w1, 4 * n, 4) * 0x00204081u) & 0x01010101u;
+  }
+}
+
 // Lane l of wave w owns the R rows ((chunk * tiles_per_chunk + w * R + r) * 64 + l),
 // r < R, and scores them together.  Each group's 128 sign bits of a row are
 // one 16-byte load; the four scales of a quad of groups are one more.  The
@@ -98,6 +115,9 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   __shared__ uint32_t last_wg;
   HeadStage& hst = csm.hs;
   head_stage_init(hst);  // ordered by the barriers below
+  // from four rows on, the activation bytes and 8-bit dot products (see
+  // spread_signs) take fewer instructions than the bit planes
+  constexpr bool kBytes = M >= 4 && R == 1;
   const int G = a.G;
   PlaneGroup* pgs = reinterpret_cast<PlaneGroup*>(dyn_lds);          // [M][G]
   int* cg = reinterpret_cast<int*>(pgs + (size_t)M * G);              // [M][G] C of the group
@@ -152,7 +172,13 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
           mine = make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1, (uint32_t)(b1 >> 32));
         cgroup += (p == 7 ? -128 : 1 << p) * (__popcll(b0) + __popcll(b1));
       }
-      if (lane < 8) pgs[mg].plane[lane] = mine;
+      if constexpr (kBytes) {  // the activation bytes themselves
+        uint8_t* slot = reinterpret_cast<uint8_t*>(&pgs[mg]);
+        slot[lane] = (uint8_t)a0;
+        slot[64 + lane] = (uint8_t)a1;
+      } else {
+        if (lane < 8) pgs[mg].plane[lane] = mine;
+      }
       if (lane == 0) cg[mg] = cgroup;
     }
   };
@@ -217,13 +243,40 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
 
   auto compute_group = [&](int g, const uint4 (&w)[R], const float (&s)[R]) {
+    if constexpr (kBytes) {
+      // two halves of 64 elements, so only 16 spread words are live at once
+      int sacc[M];
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      uint32_t u[R];
-      plane_dot<R>(w, pgs[(size_t)m * G + g].plane, u);
-      const int c = cg[m * G + g];
+      for (int m = 0; m < M; ++m) sacc[m] = 0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) acc[r][m] = fmaf((float)(2 * (int)u[r] - c), s[r], acc[r][m]);
+      for (int half = 0; half < 2; ++half) {
+        uint32_t e[16];
+        spread_signs(half ? w[0].z : w[0].x, half ? w[0].w : w[0].y, e);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const uint4* ab = pgs[(size_t)m * G + g].plane + 4 * half;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint4 av = ab[q];
+            sacc[m] = __builtin_amdgcn_sdot4((int)av.x, (int)e[4 * q], sacc[m], false);
+            sacc[m] = __builtin_amdgcn_sdot4((int)av.y, (int)e[4 * q + 1], sacc[m], false);
+            sacc[m] = __builtin_amdgcn_sdot4((int)av.z, (int)e[4 * q + 2], sacc[m], false);
+            sacc[m] = __builtin_amdgcn_sdot4((int)av.w, (int)e[4 * q + 3], sacc[m], false);
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        acc[0][m] = fmaf((float)(2 * sacc[m] - cg[m * G + g]), s[0], acc[0][m]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        uint32_t u[R];
+        plane_dot<R>(w, pgs[(size_t)m * G + g].plane, u);
+        const int c = cg[m * G + g];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][m] = fmaf((float)(2 * (int)u[r] - c), s[r], acc[r][m]);
+      }
     }
   };
   auto compute_quad = [&](int q, const uint4 (&buf)[R][4], const float4 (&s)[R]) {

@@ -142,18 +142,22 @@ def test_pack_signed_zero_and_golden_layout():
     (1, 128, 1, 1, False), (1, 128, 40, 40, True), (2, 640, 65, 7, False),
     (3, 512, 1000, 100, True), (8, 2048, 8192, 1, False), (8, 8192, 3000, 64, True),
     (4, 1024, 32001, 50, True), (1, 384, 70000, 2048, False),
+    # from four rows on the scorer uses activation bytes and 8-bit dot products
+    (5, 1280, 5000, 50, False), (6, 384, 2049, 13, True), (7, 2560, 9000, 300, False),
 ])
 def test_binary_shapes(M, H, V, k, with_bias):
     Case(M, H, V, seed=M + H + V, with_bias=with_bias).check(k)
 
 
-def test_full_int8_range_including_minus_128():
-    M, H, V = 3, 1024, 5000
+@pytest.mark.parametrize("M", [3, 6])  # bit planes, and activation bytes with dot4
+def test_full_int8_range_including_minus_128(M):
+    H, V = 1024, 5000
     rng = np.random.default_rng(4)
     act_q = rng.integers(-128, 128, size=(M, H)).astype(np.int8)
     act_q[0, :] = -128
     act_q[1, ::2] = 127
-    act_scale = np.array([1e-3, 2e-3, 0.5], dtype=np.float32)
+    act_q[M - 1, 1::2] = -128
+    act_scale = np.array([1e-3, 2e-3, 0.5, 0.25, 4e-3, 1.0][:M], dtype=np.float32)
     c = Case(M, H, V, seed=3, act=(act_q, act_scale), with_bias=True)
     c.check(50)
 
