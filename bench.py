@@ -69,6 +69,7 @@ def parse_args():
     p.add_argument("--H", type=int, default=5120)
     p.add_argument("--bias", action="store_true")
     p.add_argument("--chunk-rows", type=int, default=0)
+    p.add_argument("--lse", action="store_true", help="also return each row's log-sum-exp")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-reps", type=int, default=5, help="oracle calls timed for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -326,6 +327,7 @@ def main():
     vals = torch.empty((M, k), dtype=torch.float32, device=dev)
     idx = torch.empty((M, k), dtype=torch.int64, device=dev)
     work = lt.new_workspace(M, V, k, args.chunk_rows, device=dev)
+    lse = torch.empty(M, dtype=torch.float32, device=dev) if args.lse else None
     torch.cuda.synchronize()
     log(f"inputs ready in {time.time() - t0:.1f} s (packed head {lt.packed_bytes(V, H)} B x {args.copies})")
 
@@ -336,7 +338,7 @@ def main():
         wq, ws = copies[i % rot]
         lt.lm_head_topk_binary(d_aq, d_as, wq, ws, bias=d_b, k=k, vocab_size=V,
                                chunk_rows=args.chunk_rows, out=(vals, idx), workspace=work,
-                               score_events=ev)
+                               score_events=ev, lse=lse)
 
     for i in range(args.warmup):
         call(i, None)
@@ -390,8 +392,9 @@ def main():
         "dtype": "int8 x 1-bit integer dots, fp32 accumulate",
         "data": "synthetic (seeded N(0,1)/sqrt(H) head and hidden rows; int8 symmetric activations)",
         "config": {"workload": f"binary head V={V} H={H} k={k} M={M} group 128"
-                               f"{' +bias' if args.bias else ''}, {args.copies} rotated packed copies",
-                   "V": V, "H": H, "k": k, "M": M, "bias": bool(args.bias),
+                               f"{' +bias' if args.bias else ''}{' +lse' if args.lse else ''}, "
+                               f"{args.copies} rotated packed copies",
+                   "V": V, "H": H, "k": k, "M": M, "bias": bool(args.bias), "lse": bool(args.lse),
                    "chunk_rows": args.chunk_rows or 1024, "rotated_copies": args.copies},
         "gbps": round(head_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "head_bytes": head_bytes,

@@ -81,6 +81,15 @@ typedef struct {
      times that kernel apart from the merge kernels after it.  The events
      must exist; the library does not own them. */
   void* score_events;
+  /* If not NULL: a device array of M floats that receives, for each row,
+     the log-sum-exp of all V of its logits, log(sum_v exp(L[m, v])), so
+     that values[m, i] - lse[m] are the top-k log-probabilities (Selective
+     Log Softmax page, section "Kernel design", online log-sum-exp: per
+     slice a maximum and a sum of exponentials, then combined).  Each wave
+     of a chunk reduces its rows to one (max, sum) pair and the final merge
+     combines them; no weight byte is read twice.  An +inf logit gives +inf;
+     a row whose logits are all -inf gives -inf.  16-byte aligned. */
+  float* lse;
 } lmtopk_options;
 
 /* ------------------------------------------------------------------------ */
@@ -141,7 +150,8 @@ lmtopk_status lmtopk_packed_bytes(int64_t V, int64_t H, int32_t group_size,
    when they fit it, instead of a second launch), then, per row and chunk,
    the chunk's four best candidates and all its candidates (8 bytes each),
    plus one intermediate merge level when a row has more than 16384
-   candidates.
+   candidates, plus 8 bytes per row, chunk and wave for the log-sum-exp
+   partials.
    Errors: NULL, SHAPE, K, OPTIONS. */
 lmtopk_status lmtopk_workspace_bytes(int64_t M, int64_t V, int32_t k,
                                      const lmtopk_options* opt, size_t* bytes);

@@ -102,7 +102,9 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, Geome
     g->fused = 1;
     g->n_levels = 0;
   }
-  g->workspace_bytes = g->sync_bytes + g->heads_bytes + g->region0_bytes + g->region1_bytes;
+  g->lse_bytes = round_up((size_t)(M * g->n_chunks * g->nw * 8), 256);
+  g->workspace_bytes =
+      g->sync_bytes + g->heads_bytes + g->region0_bytes + g->region1_bytes + g->lse_bytes;
   return LMTOPK_OK;
 }
 
@@ -176,6 +178,8 @@ static lmtopk_status common_checks(const void* workspace, size_t workspace_bytes
   st = lmtopk::make_geometry(M, V, k, opt ? opt->chunk_rows : 0, g);
   if (st) return (lmtopk_status)st;
   if (!lmtopk::aligned16(values) || !lmtopk::aligned16(indices)) return LMTOPK_ERR_ALIGN;
+  g->lse = opt ? opt->lse : nullptr;
+  if (g->lse && !lmtopk::aligned16(g->lse)) return LMTOPK_ERR_ALIGN;
   if (!workspace || workspace_bytes < g->workspace_bytes) return LMTOPK_ERR_WORKSPACE;
   if (!lmtopk::aligned16(workspace)) return LMTOPK_ERR_ALIGN;
   return LMTOPK_OK;

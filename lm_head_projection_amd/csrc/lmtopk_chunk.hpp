@@ -24,6 +24,8 @@ struct ChunkOut {
   int k;
   int M;
   int fused;          // the launch's last workgroup merges (fused_merge_tail)
+  uint2* lse_part;    // log-sum-exp partials [M][n_chunks][waves], or null
+  float* lse;         // [M] or null
 };
 
 // The fused merge's view of a chunk launch's outputs.
@@ -38,6 +40,8 @@ __device__ __forceinline__ FusedMerge fused_merge_of(const ChunkOut& o) {
   f.n_chunks = o.n_chunks;
   f.kc = o.kc;
   f.k = o.k;
+  f.lse_part = o.lse_part;
+  f.lse = o.lse;
   return f;
 }
 
@@ -62,6 +66,25 @@ __device__ __forceinline__ void chunk_select_write(const float (&val)[RPL], cons
     key[r] = float_key(val[r]);
   }
   const size_t row_chunk = (size_t)m * o.n_chunks + blockIdx.x;
+  if (o.lse_part != nullptr) {
+    // this wave's (max, sum of exp(logit - max)) over its valid rows
+    const int wave = wave_id();
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+      if ((valid >> r) & 1u) mx = fmaxf(mx, val[r]);
+    mx = wave_max_f32(mx);
+    float sum = mx == INFINITY ? 1.f : 0.f;
+    if (mx != INFINITY && mx != -INFINITY) {
+#pragma unroll
+      for (int r = 0; r < RPL; ++r)
+        if ((valid >> r) & 1u) sum += expf(val[r] - mx);
+    }
+    sum = wave_sum_f32(sum);
+    if (lane_id() == 0)
+      st_cand(&o.lse_part[row_chunk * (blockDim.x >> 6) + wave],
+              make_uint2(__float_as_uint(mx), __float_as_uint(sum)));
+  }
   uint2* out = o.cand + row_chunk * o.kc;
   uint2* heads = o.heads + row_chunk * kHeads;
   if (o.k <= kWaveTops * (int)(blockDim.x >> 6)) {
@@ -140,6 +163,10 @@ inline ChunkOut chunk_out(const Geometry& g, void* workspace, float* values, int
   o.values = values;
   o.indices = indices;
   o.M = (int)g.M;
+  o.lse = g.lse;
+  o.lse_part = g.lse ? reinterpret_cast<uint2*>(ws + g.sync_bytes + g.heads_bytes + g.region0_bytes +
+                                                g.region1_bytes)
+                     : nullptr;
   return o;
 }
 }  // namespace lmtopk

@@ -100,6 +100,32 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// The same steps on fp32 values: max (identity -inf) and sum (identity 0) in
+// a fixed order, so a result does not depend on timing.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ float dpp_f32(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), kCtrl,
+                                                    kRowMask, 0xF, false));
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<kQuadSwap1>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<kQuadSwap2>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<kRowHalfMirror>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<kRowMirror>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<kRowBcast15, 0xA>(-INFINITY, v));
+  v = fmaxf(v, dpp_f32<kRowBcast31, 0xC>(-INFINITY, v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += dpp_f32<kQuadSwap1>(0.f, v);
+  v += dpp_f32<kQuadSwap2>(0.f, v);
+  v += dpp_f32<kRowHalfMirror>(0.f, v);
+  v += dpp_f32<kRowMirror>(0.f, v);
+  v += dpp_f32<kRowBcast15, 0xA>(0.f, v);
+  v += dpp_f32<kRowBcast31, 0xC>(0.f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Inclusive prefix sum over the 16 lanes of each row (Kogge-Stone, zero fill).
 __device__ __forceinline__ uint32_t row_scan_inclusive(uint32_t v) {
   v += dpp<kRowShr1, 0xF, true>(0u, v);
@@ -871,6 +897,70 @@ __device__ __forceinline__ void merge_final(const uint2* in, int64_t n_in, const
   rank_and_write(fs, n, k, values, indices);
 }
 
+// Log-sum-exp of one row (Selective Log Softmax page, section "Kernel
+// design": per-slice maxima and sums of exponentials, combined).  part[0, n)
+// holds one (max, sum) pair per wave and chunk of the row, sum = the sum of
+// exp(logit - max) over that wave's rows (max -inf: no finite rows, sum 0;
+// max +inf: an +inf logit).  With M the largest max, the row's log-sum-exp
+// is M + log(sum of pair.sum * exp(pair.max - M)); +inf if M is +inf, -inf
+// if M is -inf.  Called by the whole workgroup; sm's wave slots are reused,
+// and the reductions run in a fixed order.
+// A thread's pairs i = thread + j * blockDim (j < kLsePairs) may be loaded
+// by the caller ahead of time (load_lse_pairs), so that their round trip
+// overlaps other work; rows with more pairs are read in the loop.
+constexpr int kLsePairs = 4;
+__device__ __forceinline__ bool load_lse_pairs(const uint2* part, int n, uint2 (&p)[kLsePairs]) {
+  const bool fits = n <= kLsePairs * (int)blockDim.x;
+#pragma unroll
+  for (int j = 0; j < kLsePairs; ++j) {
+    const int i = (int)threadIdx.x + j * (int)blockDim.x;
+    p[j] = fits && i < n ? ld_cand(&part[i]) : make_uint2(__float_as_uint(-INFINITY), 0u);
+  }
+  return fits;
+}
+
+__device__ __forceinline__ void merge_lse(const uint2* part, int n, float* out, SelectSmem& sm,
+                                          bool have, const uint2 (&pre)[kLsePairs]) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  const int nw = blockDim.x >> 6;
+  float mx = -INFINITY;
+  if (have) {
+#pragma unroll
+    for (int j = 0; j < kLsePairs; ++j) mx = fmaxf(mx, __uint_as_float(pre[j].x));
+  } else {
+    for (int i = tid; i < n; i += (int)blockDim.x) mx = fmaxf(mx, __uint_as_float(ld_cand(&part[i]).x));
+  }
+  mx = wave_max_f32(mx);
+  if (lane == 0) sm.wmax[wave] = __float_as_uint(mx);
+  lds_barrier();
+  float M = -INFINITY;
+  for (int w = 0; w < nw; ++w) M = fmaxf(M, __uint_as_float(sm.wmax[w]));
+  float sum = 0.f;
+  auto add = [&](const uint2& p) {
+    const float pm = __uint_as_float(p.x);
+    if (pm != -INFINITY) sum += __uint_as_float(p.y) * expf(pm - M);
+  };
+  if (M != INFINITY && M != -INFINITY) {
+    if (have) {
+#pragma unroll
+      for (int j = 0; j < kLsePairs; ++j) add(pre[j]);
+    } else {
+      for (int i = tid; i < n; i += (int)blockDim.x) add(ld_cand(&part[i]));
+    }
+  }
+  sum = wave_sum_f32(sum);
+  if (lane == 0) sm.wmin[wave] = __float_as_uint(sum);
+  lds_barrier();
+  if (tid == 0) {
+    float S = 0.f;
+    for (int w = 0; w < nw; ++w) S += __uint_as_float(sm.wmin[w]);
+    *out = M == INFINITY ? INFINITY : M == -INFINITY ? -INFINITY : M + logf(S);
+  }
+  lds_barrier();  // sm is reused
+}
+
 // LDS of a chunk kernel: the chunk selection's staging, and, after it, the
 // final merge of the fused path.
 union ChunkSmem {
@@ -890,6 +980,8 @@ struct FusedMerge {
   int n_chunks;
   int kc;
   int k;
+  const uint2* lse_part;  // [M][n_chunks][waves] (max, sum) pairs, or null
+  float* lse;             // [M] or null
 };
 
 // Fused second pass (lm-head-topk page, section "Method": the chunk
@@ -914,11 +1006,18 @@ __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem
   lds_barrier();
   if (uniform(last) == 0u) return;
   const int64_t n_in = (int64_t)f.n_chunks * f.kc;
+  const int n_part = f.n_chunks * (int)(blockDim.x >> 6);
   for (int m = 0; m < f.M; ++m) {
+    // the row's log-sum-exp partials are requested before the merge, which
+    // waits for its own loads meanwhile
+    uint2 pre[kLsePairs];
+    bool have = false;
+    if (f.lse != nullptr) have = load_lse_pairs(f.lse_part + (size_t)m * n_part, n_part, pre);
     merge_final<RM>(f.cand + (size_t)m * n_in, n_in, f.heads + (size_t)m * f.n_chunks * kHeads,
                     f.n_chunks, f.kc, (uint32_t)f.k, f.values + (size_t)m * f.k,
                     f.indices + (size_t)m * f.k, (int)blockDim.x, sm, fs);
     lds_barrier();  // fs is reused by the next row
+    if (f.lse != nullptr) merge_lse(f.lse_part + (size_t)m * n_part, n_part, f.lse + m, sm, have, pre);
   }
   if (threadIdx.x == 0) __hip_atomic_store(f.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -36,7 +36,9 @@ struct Geometry {
   size_t heads_bytes;    // best candidates of each chunk [M][n_chunks][4] x 8 B
   size_t region0_bytes;  // chunk candidates [M][n_chunks * kc] x 8 B
   size_t region1_bytes;  // first intermediate merge output, or 0
+  size_t lse_bytes;      // log-sum-exp partials [M][n_chunks][nw] x (max, sum)
   size_t workspace_bytes;
+  float* lse;            // this call's log-sum-exp output [M], or null (not part of the plan)
 };
 
 // Returns 0 or an lmtopk_status code (SHAPE, K, OPTIONS).

@@ -136,6 +136,9 @@ struct MergeArgs {
   uint2* out;       // intermediate: [M][n_seg][k]
   float* values;    // final: [M][k]
   int64_t* indices; // final: [M][k]
+  const uint2* lse_part;  // final: log-sum-exp partials [M][n_part], or null
+  int n_part;
+  float* lse;             // final: [M] or null
 };
 
 // Workgroup (segment s, row m) takes candidates [s*seg, (s+1)*seg) of row m,
@@ -151,9 +154,16 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
   const uint2* in = a.in + (size_t)m * a.n_in;
   if (a.n_seg == 1) {
     __shared__ FinalSmem fs;
+    uint2 pre[kLsePairs];
+    bool have = false;
+    if (a.lse != nullptr) have = load_lse_pairs(a.lse_part + (size_t)m * a.n_part, a.n_part, pre);
     merge_final<RM>(in, a.n_in, a.heads ? a.heads + (size_t)m * a.n_max * kHeads : nullptr,
                     a.n_max, a.kc, (uint32_t)a.k, a.values + (size_t)m * a.k, a.indices + (size_t)m * a.k,
                     a.threads, ssm, fs);
+    if (a.lse != nullptr) {
+      lds_barrier();  // ssm is reused
+      merge_lse(a.lse_part + (size_t)m * a.n_part, a.n_part, a.lse + m, ssm, have, pre);
+    }
     return;
   }
   const int wave = wave_id();
@@ -265,6 +275,9 @@ int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* in
     a.out = regions[(l + 1) & 1];
     a.values = values;
     a.indices = indices;
+    a.lse = g.lse;
+    a.n_part = g.n_chunks * g.nw;
+    a.lse_part = reinterpret_cast<const uint2*>(ws + g.region0_bytes + g.region1_bytes);
     auto kern = merge_kernel(L.rm);
     if (!kern) return (int)hipErrorInvalidValue;
     const hipError_t e = launch1(kern, dim3(L.n_seg, (unsigned)g.M), dim3(64 * L.nw), 0, stream, a);

@@ -18,6 +18,8 @@ Modules
   packing     -- logical sign/scale packing of a dense head, and this
                  library's packed byte layout (version 1) written and read by
                  the oracle's own code from the layout's specification.
+  normalizer  -- log-sum-exp of each row (the normalizer of the top-k
+                 log-probabilities).
 """
 
 from .projection import (
@@ -27,6 +29,7 @@ from .projection import (
     project_dense,
 )
 from .select import certify_topk, float_key_order, topk_stable, topk_stable_rows
+from .normalizer import logsumexp_row, logsumexp_rows
 from .packing import (
     pack_layout_bytes,
     pack_logical,
@@ -41,6 +44,8 @@ __all__ = [
     "project_dense",
     "certify_topk",
     "float_key_order",
+    "logsumexp_row",
+    "logsumexp_rows",
     "topk_stable",
     "topk_stable_rows",
     "pack_layout_bytes",

@@ -45,12 +45,13 @@ def test_layout_and_sizes():
     assert lt.packed_bytes(32001, 2048) == (32064 * 2048 // 8, 32064 * 16 * 4)
     assert lt.packed_bytes(1, 640) == (64 * 640 // 8, 64 * 8 * 4)   # G=5 pads to 8 scales
     # completion counter (256 B) + chunk heads (243 x 4 x 8 B rounded to 256) + chunk
-    # candidates of the flagship (243 chunks x 50 x 8 B rounded to 256); one workgroup
-    # merges them, no second region
-    assert lt.workspace_bytes(1, 248320, 50) == 256 + 7936 + 97280
+    # candidates of the flagship (243 chunks x 50 x 8 B rounded to 256) + log-sum-exp
+    # partials (243 chunks x 16 waves x 8 B, rounded to 256); one workgroup merges
+    # them, no second region
+    assert lt.workspace_bytes(1, 248320, 50) == 256 + 7936 + 97280 + 31232
     # k >= chunk rows: every chunk offers all its rows, and the merge needs two levels
     assert lt.workspace_bytes(8, 248320, 1024) == (256 + 8 * 243 * 32 + 8 * 243 * 1024 * 8
-                                                   + 8 * 16 * 1024 * 8)
+                                                   + 8 * 16 * 1024 * 8 + 8 * 243 * 16 * 8)
 
 
 def test_status_strings():

@@ -329,3 +329,43 @@ def test_generators_deterministic_and_thread_independent():
     bits = synthetic.f32_to_bf16_bits(np.array([1.0, 1.00390625, 1.01171875, -2.5], np.float32))
     # 1 + 2^-8 is halfway between bf16 neighbours 1 and 1 + 2^-7: ties to even -> 1.0
     assert list(bits) == [0x3F80, 0x3F80, 0x3F82, 0xC020]
+
+
+# ---------------------------------------------------------------------------
+# log-sum-exp (Selective Log Softmax page: log-probability = logit - lse)
+# ---------------------------------------------------------------------------
+def test_logsumexp_closed_forms():
+    # V equal logits c: lse = c + log(V); one logit: lse = that logit
+    for V in (1, 2, 7, 1000, 248320):
+        for c in (0.0, -3.5, 12.25):
+            assert math.isclose(oracle.logsumexp_row(np.full(V, c)), c + math.log(V),
+                                rel_tol=0, abs_tol=1e-12 * max(1.0, abs(c) + math.log(V)))
+    assert oracle.logsumexp_row(np.array([-7.25])) == -7.25
+    # two entries a, b: lse = max + log1p(exp(-|a - b|))
+    for a, b in ((1.0, 2.0), (-30.0, 5.0), (0.5, 0.5)):
+        want = max(a, b) + math.log1p(math.exp(-abs(a - b)))
+        assert math.isclose(oracle.logsumexp_row(np.array([a, b])), want, rel_tol=1e-15, abs_tol=1e-15)
+
+
+def test_logsumexp_brute_force_and_shift():
+    rng = np.random.default_rng(11)
+    x = rng.normal(0.0, 2.0, size=513)
+    # the plain log of the plain sum (no overflow at this scale), summed exactly
+    brute = math.log(math.fsum(math.exp(v) for v in x))
+    assert math.isclose(oracle.logsumexp_row(x), brute, rel_tol=1e-14, abs_tol=1e-14)
+    # shift invariance far outside the range exp can represent unshifted
+    for c in (-1000.0, 700.0, 1e4):
+        assert math.isclose(oracle.logsumexp_row(x + c), brute + c, rel_tol=1e-13, abs_tol=1e-10)
+
+
+def test_logsumexp_matches_an_independent_routine_and_infinities():
+    scipy_special = pytest.importorskip("scipy.special")
+    rng = np.random.default_rng(12)
+    L = rng.normal(0.0, 3.0, size=(4, 2049)).astype(np.float32)
+    got = oracle.logsumexp_rows(L)
+    want = scipy_special.logsumexp(L.astype(np.float64), axis=1)
+    assert np.allclose(got, want, rtol=1e-14, atol=1e-14)
+    row = np.array([0.0, -np.inf, 3.0])
+    assert math.isclose(oracle.logsumexp_row(row), 3.0 + math.log1p(math.exp(-3.0)), rel_tol=1e-15)
+    assert oracle.logsumexp_row(np.array([1.0, np.inf, -np.inf])) == np.inf
+    assert oracle.logsumexp_row(np.full(5, -np.inf)) == -np.inf
