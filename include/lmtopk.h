@@ -90,6 +90,14 @@ typedef struct {
      combines them; no weight byte is read twice.  An +inf logit gives +inf;
      a row whose logits are all -inf gives -inf.  16-byte aligned. */
   float* lse;
+  /* If not NULL: a device bitmask [M][ceil(V / 32)] of int32 words; bit
+     (v % 32) of word v / 32 of row m is 1 if vocabulary entry v is allowed
+     (logits-processor page, section "API": a grammar's bitmask, bit 1 =
+     allowed, disallowed logits set to -inf).  A disallowed entry's logit
+     counts as -inf, for the top-k and for lse alike: it is returned only
+     when fewer than k entries are allowed, after every allowed one, in index
+     order.  Bits past V are ignored.  16-byte aligned. */
+  const int32_t* allowed;
 } lmtopk_options;
 
 /* ------------------------------------------------------------------------ */

@@ -56,7 +56,8 @@ class LmTopkError(ValueError):
 
 class _Options(ctypes.Structure):
     _fields_ = [("chunk_rows", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("score_events", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
+                ("score_events", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("allowed", ctypes.c_void_p)]
 
 
 def _load():
@@ -110,18 +111,29 @@ def packed_bytes(V, H, group_size=GROUP_SIZE):
     return a.value, b.value
 
 
-def _opts(chunk_rows, score_events=None, lse=None):
+def _opts(chunk_rows, score_events=None, lse=None, allowed=None):
     """score_events: None or (start, stop) hipEvent_t handles recorded at the
     scoring kernel's start and end.  lse: None or a float32 [M] GPU tensor
-    that receives each row's log-sum-exp."""
+    that receives each row's log-sum-exp.  allowed: None or an int32
+    [M, ceil(V/32)] GPU bitmask (bit 1 = allowed)."""
     lp = lse.data_ptr() if lse is not None else None
+    ap = allowed.data_ptr() if allowed is not None else None
     if score_events is None:
-        return _Options(int(chunk_rows), 0, None, lp)
+        return _Options(int(chunk_rows), 0, None, lp, ap)
     start, stop = (e.value if isinstance(e, ctypes.c_void_p) else int(e) for e in score_events)
     arr = (ctypes.c_void_p * 2)(start, stop)
-    o = _Options(int(chunk_rows), 0, ctypes.cast(arr, ctypes.c_void_p), lp)
+    o = _Options(int(chunk_rows), 0, ctypes.cast(arr, ctypes.c_void_p), lp, ap)
     o._events = arr  # keep the array alive as long as the options
     return o
+
+
+def _allowed_in(allowed, M, V):
+    if allowed is None:
+        return None
+    _need_cuda("allowed", allowed, torch.int32, 2)
+    if tuple(allowed.shape) != (M, (V + 31) // 32):
+        raise ValueError("allowed must be int32 [M, ceil(V / 32)]")
+    return allowed
 
 
 def _lse_out(lse, M):
@@ -223,14 +235,16 @@ def pack_binary(weight, group_size=GROUP_SIZE):
 
 def lm_head_topk_binary(act_q, act_scale, wq, wscale, bias=None, group_size=GROUP_SIZE, k=50, *,
                         vocab_size=None, chunk_rows=0, out=None, workspace=None,
-                        score_events=None, lse=None):
+                        score_events=None, lse=None, allowed=None):
     """Exact top-k of the binary-head logits of each activation row.
 
     act_q int8 [M, H]; act_scale float32 [M]; (wq, wscale) from pack_binary;
     bias float32 [V] or None.  vocab_size V is required when bias is None
     (the packed arrays are padded to whole 64-row tiles).  lse: optional
     float32 [M] GPU tensor that receives each row's log-sum-exp over all V
-    logits (values - lse are the top-k log-probabilities).
+    logits (values - lse are the top-k log-probabilities).  allowed:
+    optional int32 [M, ceil(V/32)] bitmask, bit 1 = allowed; a disallowed
+    entry's logit counts as -inf.
     """
     _need_cuda("act_q", act_q, torch.int8, 2)
     _need_cuda("act_scale", act_scale, torch.float32, 1)
@@ -254,7 +268,7 @@ def lm_head_topk_binary(act_q, act_scale, wq, wscale, bias=None, group_size=GROU
     dev = act_q.device
     values, indices = _outputs(dev, M, k, out)
     ws = _workspace(dev, M, V, k, chunk_rows, workspace)
-    o = _opts(chunk_rows, score_events, _lse_out(lse, M))
+    o = _opts(chunk_rows, score_events, _lse_out(lse, M), _allowed_in(allowed, M, V))
     _check(_lib.lmtopk_binary(_ptr(act_q), _ptr(act_scale), _ptr(wq), _ptr(wscale), _ptr(bias),
                               M, V, H, group_size, k, _ptr(values), _ptr(indices), _ptr(ws),
                               ws.numel(), ctypes.byref(o), _stream(act_q)))
@@ -262,9 +276,10 @@ def lm_head_topk_binary(act_q, act_scale, wq, wscale, bias=None, group_size=GROU
 
 
 def lm_head_topk_dense(hidden, weight, k=50, bias=None, *, chunk_rows=0, out=None,
-                       workspace=None, score_events=None, lse=None):
+                       workspace=None, score_events=None, lse=None, allowed=None):
     """Exact top-k of hidden @ weight.T (+ bias); hidden and weight both fp32 or both bf16.
-    lse: optional float32 [M] GPU tensor for each row's log-sum-exp."""
+    lse: optional float32 [M] GPU tensor for each row's log-sum-exp; allowed:
+    optional int32 [M, ceil(V/32)] bitmask (bit 1 = allowed)."""
     _need_cuda("hidden", hidden, ndim=2)
     _need_cuda("weight", weight, ndim=2)
     if hidden.dtype != weight.dtype or hidden.dtype not in (torch.float32, torch.bfloat16):
@@ -280,7 +295,7 @@ def lm_head_topk_dense(hidden, weight, k=50, bias=None, *, chunk_rows=0, out=Non
     dev = hidden.device
     values, indices = _outputs(dev, M, k, out)
     ws = _workspace(dev, M, V, k, chunk_rows, workspace)
-    o = _opts(chunk_rows, score_events, _lse_out(lse, M))
+    o = _opts(chunk_rows, score_events, _lse_out(lse, M), _allowed_in(allowed, M, V))
     dt = _BF16 if hidden.dtype == torch.bfloat16 else _F32
     _check(_lib.lmtopk_dense(_ptr(hidden), _ptr(weight), dt, _ptr(bias), M, V, H, k,
                              _ptr(values), _ptr(indices), _ptr(ws), ws.numel(), ctypes.byref(o),
@@ -289,9 +304,10 @@ def lm_head_topk_dense(hidden, weight, k=50, bias=None, *, chunk_rows=0, out=Non
 
 
 def topk_logits(logits, k, *, chunk_rows=0, out=None, workspace=None, score_events=None,
-                lse=None):
+                lse=None, allowed=None):
     """The selection stage alone: exact top-k of each row of fp32 logits [M, V].
-    lse: optional float32 [M] GPU tensor for each row's log-sum-exp."""
+    lse: optional float32 [M] GPU tensor for each row's log-sum-exp; allowed:
+    optional int32 [M, ceil(V/32)] bitmask (bit 1 = allowed)."""
     if not isinstance(logits, torch.Tensor) or logits.device.type != "cuda":
         raise ValueError("logits must be a GPU tensor")
     if logits.dtype != torch.float32 or logits.dim() != 2 or logits.stride(1) != 1:
@@ -301,7 +317,7 @@ def topk_logits(logits, k, *, chunk_rows=0, out=None, workspace=None, score_even
     dev = logits.device
     values, indices = _outputs(dev, M, k, out)
     ws = _workspace(dev, M, V, k, chunk_rows, workspace)
-    o = _opts(chunk_rows, score_events, _lse_out(lse, M))
+    o = _opts(chunk_rows, score_events, _lse_out(lse, M), _allowed_in(allowed, M, V))
     _check(_lib.lmtopk_select(_ptr(logits), M, V, ld, k, _ptr(values), _ptr(indices), _ptr(ws),
                               ws.numel(), ctypes.byref(o), _stream(logits)))
     return values, indices

@@ -180,6 +180,8 @@ static lmtopk_status common_checks(const void* workspace, size_t workspace_bytes
   if (!lmtopk::aligned16(values) || !lmtopk::aligned16(indices)) return LMTOPK_ERR_ALIGN;
   g->lse = opt ? opt->lse : nullptr;
   if (g->lse && !lmtopk::aligned16(g->lse)) return LMTOPK_ERR_ALIGN;
+  g->allowed = opt ? opt->allowed : nullptr;
+  if (g->allowed && !lmtopk::aligned16(g->allowed)) return LMTOPK_ERR_ALIGN;
   if (!workspace || workspace_bytes < g->workspace_bytes) return LMTOPK_ERR_WORKSPACE;
   if (!lmtopk::aligned16(workspace)) return LMTOPK_ERR_ALIGN;
   return LMTOPK_OK;

@@ -209,6 +209,18 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   // hold up the barrier below, which waits for every scalar load, by a full
   // memory round trip)
   const float act_sv = a.act_scale[lane < M ? lane : M - 1];
+  // the call's bitmask bits of this lane's rows, per activation row
+  uint32_t allow[M];
+  {
+    int64_t rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t v = (tile0 + r) * 64 + lane;
+      rows[r] = v < a.V ? v : a.V - 1;
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) allow[m] = allowed_bits<R>(a.out, m, rows, a.act_scale);
+  }
   __builtin_amdgcn_sched_barrier(0);
   // (no barrier here: each wave requests its weights as soon as it has
   // requested its activation bytes, so HBM is busy from the first waves on)
@@ -359,7 +371,7 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     float val[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) val[r] = fmaf(acc[r][m], s, bias_v[r]);
-    chunk_select_write<R>(val, idx, valid, m, a.out, ssm, hst, m == M - 1);
+    chunk_select_write<R>(val, idx, valid, m, a.out, ssm, hst, m == M - 1, allow[m]);
   }
   if (a.out.fused) fused_merge_tail<kFusedRM>(fused_merge_of(a.out), ssm, csm.fs, last_wg);
 }

@@ -26,6 +26,8 @@ struct ChunkOut {
   int fused;          // the launch's last workgroup merges (fused_merge_tail)
   uint2* lse_part;    // log-sum-exp partials [M][n_chunks][waves], or null
   float* lse;         // [M] or null
+  const int32_t* allowed;  // bitmask [M][allowed_words] (bit 1 = allowed), or null
+  int allowed_words;       // ceil(V / 32)
 };
 
 // The fused merge's view of a chunk launch's outputs.
@@ -55,13 +57,39 @@ constexpr int kFusedRM = 16;
 // up): radix select, candidates in ascending index order.  Either order keeps
 // equal values in ascending index, which is all the merge relies on.  `last`
 // = no further row follows in this workgroup.
+// Bit r: vocabulary row v = rows[r] of activation row m is allowed by the
+// call's bitmask (always, without one).  rows[r] must be < V; the loads are
+// unconditional (from a valid dummy address without a mask), so a caller
+// may issue them among loads whose count must not vary.
 template <int RPL>
-__device__ __forceinline__ void chunk_select_write(const float (&val)[RPL], const int32_t (&idx)[RPL],
+__device__ __forceinline__ uint32_t allowed_bits(const ChunkOut& o, int m, const int64_t (&rows)[RPL],
+                                                 const void* dummy) {
+  uint32_t w[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) {
+    const int32_t* p = o.allowed != nullptr
+                           ? o.allowed + (size_t)m * o.allowed_words + (rows[r] >> 5)
+                           : static_cast<const int32_t*>(dummy);
+    w[r] = (uint32_t)*p;
+  }
+  uint32_t bits = 0u;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r)
+    bits |= (o.allowed == nullptr ? 1u : (w[r] >> (rows[r] & 31)) & 1u) << r;
+  return bits;
+}
+
+// `allow` bit r clear: row r's logit counts as -inf (a disallowed entry).
+template <int RPL>
+__device__ __forceinline__ void chunk_select_write(const float (&val_in)[RPL], const int32_t (&idx)[RPL],
                                                    uint32_t valid, int m, const ChunkOut& o,
-                                                   SelectSmem& sm, HeadStage& st, bool last) {
+                                                   SelectSmem& sm, HeadStage& st, bool last,
+                                                   uint32_t allow = 0xFFFFFFFFu) {
+  float val[RPL];
   uint32_t key[RPL], vb[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
+    val[r] = ((allow >> r) & 1u) ? val_in[r] : -INFINITY;
     vb[r] = __float_as_uint(val[r]);
     key[r] = float_key(val[r]);
   }
@@ -164,6 +192,8 @@ inline ChunkOut chunk_out(const Geometry& g, void* workspace, float* values, int
   o.indices = indices;
   o.M = (int)g.M;
   o.lse = g.lse;
+  o.allowed = g.allowed;
+  o.allowed_words = (int)((g.V + 31) / 32);
   o.lse_part = g.lse ? reinterpret_cast<uint2*>(ws + g.sync_bytes + g.heads_bytes + g.region0_bytes +
                                                 g.region1_bytes)
                      : nullptr;

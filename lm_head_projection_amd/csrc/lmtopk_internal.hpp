@@ -39,6 +39,7 @@ struct Geometry {
   size_t lse_bytes;      // log-sum-exp partials [M][n_chunks][nw] x (max, sum)
   size_t workspace_bytes;
   float* lse;            // this call's log-sum-exp output [M], or null (not part of the plan)
+  const int32_t* allowed;  // this call's bitmask [M][ceil(V/32)], or null (not part of the plan)
 };
 
 // Returns 0 or an lmtopk_status code (SHAPE, K, OPTIONS).

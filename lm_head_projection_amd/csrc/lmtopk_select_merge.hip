@@ -116,7 +116,11 @@ __global__ __launch_bounds__(1024) void k_select_chunk(SelectArgs a) {
     float val[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r) val[r] = ((valid >> r) & 1u) ? ld_stream(&row[idx[r]]) : 0.f;
-    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm, hst, m == (int)a.M - 1);
+    int64_t rows[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) rows[r] = ((valid >> r) & 1u) ? (int64_t)idx[r] : 0;
+    const uint32_t allow = allowed_bits<RPL>(a.out, m, rows, a.logits);
+    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm, hst, m == (int)a.M - 1, allow);
   }
   if (a.out.fused) fused_merge_tail<kFusedRM>(fused_merge_of(a.out), ssm, csm.fs, last_wg);
 }

@@ -20,6 +20,7 @@ Modules
                  the oracle's own code from the layout's specification.
   normalizer  -- log-sum-exp of each row (the normalizer of the top-k
                  log-probabilities).
+  mask        -- a grammar bitmask applied to logits (disallowed -> -inf).
 """
 
 from .projection import (
@@ -30,6 +31,7 @@ from .projection import (
 )
 from .select import certify_topk, float_key_order, topk_stable, topk_stable_rows
 from .normalizer import logsumexp_row, logsumexp_rows
+from .mask import allowed_bool, apply_allowed
 from .packing import (
     pack_layout_bytes,
     pack_logical,
@@ -45,6 +47,8 @@ __all__ = [
     "certify_topk",
     "float_key_order",
     "logsumexp_row",
+    "allowed_bool",
+    "apply_allowed",
     "logsumexp_rows",
     "topk_stable",
     "topk_stable_rows",

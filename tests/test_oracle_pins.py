@@ -369,3 +369,35 @@ def test_logsumexp_matches_an_independent_routine_and_infinities():
     assert math.isclose(oracle.logsumexp_row(row), 3.0 + math.log1p(math.exp(-3.0)), rel_tol=1e-15)
     assert oracle.logsumexp_row(np.array([1.0, np.inf, -np.inf])) == np.inf
     assert oracle.logsumexp_row(np.full(5, -np.inf)) == -np.inf
+
+
+# ---------------------------------------------------------------------------
+# grammar bitmask (logits-processor page: bit 1 = allowed, disallowed -> -inf)
+# ---------------------------------------------------------------------------
+def test_mask_hand_worked_words():
+    # word 0 = 0b101 allows entries 0 and 2; word 1 bit 0 allows entry 32; bit 31
+    # of word 0 (a negative int32) allows entry 31; bits past V are ignored
+    V = 34
+    bm = np.array([[0b101 | -2**31, 0b1 | 0b100]], dtype=np.int32)
+    allowed = oracle.allowed_bool(bm, V)
+    assert sorted(np.flatnonzero(allowed[0]).tolist()) == [0, 2, 31, 32]
+    L = np.arange(V, dtype=np.float32)[None, :]
+    out = oracle.apply_allowed(L, bm)
+    assert out[0, 2] == 2.0 and out[0, 32] == 32.0 and out[0, 1] == -np.inf and out[0, 33] == -np.inf
+    assert L[0, 1] == 1.0  # the input is not modified
+
+
+def test_mask_all_and_none_and_independent_packing():
+    rng = np.random.default_rng(21)
+    M, V = 3, 1000
+    L = rng.normal(size=(M, V)).astype(np.float32)
+    W = (V + 31) // 32
+    assert np.array_equal(oracle.apply_allowed(L, np.full((M, W), -1, dtype=np.int32)), L)
+    assert np.all(oracle.apply_allowed(L, np.zeros((M, W), dtype=np.int32)) == -np.inf)
+    want = rng.random((M, V)) < 0.3
+    # NumPy's own little-endian bit packing, read as little-endian int32 words
+    padded = np.zeros((M, W * 32), dtype=bool)
+    padded[:, :V] = want
+    bm = np.packbits(padded, axis=1, bitorder="little").view("<i4")
+    assert np.array_equal(oracle.allowed_bool(bm, V), want)
+    assert np.array_equal(oracle.apply_allowed(L, bm), np.where(want, L, -np.inf).astype(np.float32))
