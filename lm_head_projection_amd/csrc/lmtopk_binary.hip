@@ -107,7 +107,7 @@ static_assert(sizeof(SelectSmem) + sizeof(ChunkSmem) + 16 <= kChunkStaticLds,
 // Quads of weight loads in flight per wave.
 constexpr int kQuadBuffers = 2;
 
-template <int M, int R>
+template <int M, int R, bool kExtras>
 __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs a) {
   extern __shared__ __align__(16) uint8_t dyn_lds[];
   __shared__ SelectSmem ssm;
@@ -219,7 +219,8 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
       rows[r] = v < a.V ? v : a.V - 1;
     }
 #pragma unroll
-    for (int m = 0; m < M; ++m) allow[m] = allowed_bits<R>(a.out, m, rows, a.act_scale);
+    for (int m = 0; m < M; ++m)
+      allow[m] = kExtras ? allowed_bits<R>(a.out, m, rows, a.act_scale) : 0xFFFFFFFFu;
   }
   __builtin_amdgcn_sched_barrier(0);
   // (no barrier here: each wave requests its weights as soon as it has
@@ -371,31 +372,33 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     float val[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) val[r] = fmaf(acc[r][m], s, bias_v[r]);
-    chunk_select_write<R>(val, idx, valid, m, a.out, ssm, hst, m == M - 1, allow[m]);
+    chunk_select_write<R, kExtras>(val, idx, valid, m, a.out, ssm, hst, m == M - 1, allow[m]);
   }
-  if (a.out.fused) fused_merge_tail<kFusedRM>(fused_merge_of(a.out), ssm, csm.fs, last_wg);
+  if (a.out.fused) fused_merge_tail<kFusedRM, kExtras>(fused_merge_of(a.out), ssm, csm.fs, last_wg);
 }
 namespace {
 
+// kExtras: a log-sum-exp output or a bitmask (kernels without them leave
+// that code out)
 template <int M>
-void (*binary_kernel_m(int rpl))(BinaryArgs) {
+void (*binary_kernel_m(int rpl, bool extras))(BinaryArgs) {
   switch (rpl) {
-    case 1: return k_binary_chunk<M, 1>;
-    case 4: return k_binary_chunk<M, 4>;
+    case 1: return extras ? k_binary_chunk<M, 1, true> : k_binary_chunk<M, 1, false>;
+    case 4: return extras ? k_binary_chunk<M, 4, true> : k_binary_chunk<M, 4, false>;
   }
   return nullptr;
 }
 
-void (*binary_kernel(int M, int rpl))(BinaryArgs) {
+void (*binary_kernel(int M, int rpl, bool extras))(BinaryArgs) {
   switch (M) {
-    case 1: return binary_kernel_m<1>(rpl);
-    case 2: return binary_kernel_m<2>(rpl);
-    case 3: return binary_kernel_m<3>(rpl);
-    case 4: return binary_kernel_m<4>(rpl);
-    case 5: return binary_kernel_m<5>(rpl);
-    case 6: return binary_kernel_m<6>(rpl);
-    case 7: return binary_kernel_m<7>(rpl);
-    case 8: return binary_kernel_m<8>(rpl);
+    case 1: return binary_kernel_m<1>(rpl, extras);
+    case 2: return binary_kernel_m<2>(rpl, extras);
+    case 3: return binary_kernel_m<3>(rpl, extras);
+    case 4: return binary_kernel_m<4>(rpl, extras);
+    case 5: return binary_kernel_m<5>(rpl, extras);
+    case 6: return binary_kernel_m<6>(rpl, extras);
+    case 7: return binary_kernel_m<7>(rpl, extras);
+    case 8: return binary_kernel_m<8>(rpl, extras);
   }
   return nullptr;
 }
@@ -422,7 +425,7 @@ int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* ac
   a.Q = (a.G + 3) / 4;
   a.tiles_per_chunk = g.chunk_rows / 64;
   a.out = chunk_out(g, workspace, values, indices);
-  auto kern = binary_kernel((int)g.M, g.rpl);
+  auto kern = binary_kernel((int)g.M, g.rpl, g.lse != nullptr || g.allowed != nullptr);
   if (!kern) return (int)hipErrorInvalidValue;
   return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), binary_lds_bytes(g.M, H), stream, a,
                       events);

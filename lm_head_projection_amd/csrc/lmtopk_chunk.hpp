@@ -80,7 +80,9 @@ __device__ __forceinline__ uint32_t allowed_bits(const ChunkOut& o, int m, const
 }
 
 // `allow` bit r clear: row r's logit counts as -inf (a disallowed entry).
-template <int RPL>
+// kExtras false: the call has neither a log-sum-exp output nor a bitmask,
+// and that code is left out.
+template <int RPL, bool kExtras = true>
 __device__ __forceinline__ void chunk_select_write(const float (&val_in)[RPL], const int32_t (&idx)[RPL],
                                                    uint32_t valid, int m, const ChunkOut& o,
                                                    SelectSmem& sm, HeadStage& st, bool last,
@@ -89,12 +91,12 @@ __device__ __forceinline__ void chunk_select_write(const float (&val_in)[RPL], c
   uint32_t key[RPL], vb[RPL];
 #pragma unroll
   for (int r = 0; r < RPL; ++r) {
-    val[r] = ((allow >> r) & 1u) ? val_in[r] : -INFINITY;
+    val[r] = (!kExtras || ((allow >> r) & 1u)) ? val_in[r] : -INFINITY;
     vb[r] = __float_as_uint(val[r]);
     key[r] = float_key(val[r]);
   }
   const size_t row_chunk = (size_t)m * o.n_chunks + blockIdx.x;
-  if (o.lse_part != nullptr) {
+  if (kExtras && o.lse_part != nullptr) {
     // this wave's (max, sum of exp(logit - max)) over its valid rows
     const int wave = wave_id();
     float mx = -INFINITY;

@@ -992,7 +992,9 @@ struct FusedMerge {
 // counter; the workgroup that counts last sees every chunk's candidates and
 // merges all M rows, then sets the counter back to zero for the next call.
 // n_chunks * kc <= blockDim.x * RM.
-template <int RM>
+// kExtras false: the launch has neither a log-sum-exp output nor a bitmask,
+// and that code is left out.
+template <int RM, bool kExtras = true>
 __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem& sm, FinalSmem& fs,
                                  uint32_t& last) {
   // every store of this thread has been acknowledged (gfx9 counts stores in vmcnt)
@@ -1012,12 +1014,13 @@ __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem
     // waits for its own loads meanwhile
     uint2 pre[kLsePairs];
     bool have = false;
-    if (f.lse != nullptr) have = load_lse_pairs(f.lse_part + (size_t)m * n_part, n_part, pre);
+    if (kExtras && f.lse != nullptr) have = load_lse_pairs(f.lse_part + (size_t)m * n_part, n_part, pre);
     merge_final<RM>(f.cand + (size_t)m * n_in, n_in, f.heads + (size_t)m * f.n_chunks * kHeads,
                     f.n_chunks, f.kc, (uint32_t)f.k, f.values + (size_t)m * f.k,
                     f.indices + (size_t)m * f.k, (int)blockDim.x, sm, fs);
     lds_barrier();  // fs is reused by the next row
-    if (f.lse != nullptr) merge_lse(f.lse_part + (size_t)m * n_part, n_part, f.lse + m, sm, have, pre);
+    if (kExtras && f.lse != nullptr)
+      merge_lse(f.lse_part + (size_t)m * n_part, n_part, f.lse + m, sm, have, pre);
   }
   if (threadIdx.x == 0) __hip_atomic_store(f.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
