@@ -143,7 +143,8 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   // before the weight prefetch, and the prefetch is followed only by
   // straight-line code, so the waits after it cover exactly what they need.
   // 1. bit planes of a batch of groups: each plane word is one ballot over
-  //    64 activations (groups b0, b0 + nw, ..., this wave's share)
+  //    64 activations (groups b0, b0 + nw, ..., this wave's share); from
+  //    four rows on the group's activation bytes themselves (kBytes)
   constexpr int kBatch = 4;
   const int n_mg = M * G;
   auto load_acts = [&](int b0, int8_t (&y0)[kBatch], int8_t (&y1)[kBatch]) {
