@@ -121,7 +121,6 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   const int G = a.G;
   PlaneGroup* pgs = reinterpret_cast<PlaneGroup*>(dyn_lds);          // [M][G]
   int* cg = reinterpret_cast<int*>(pgs + (size_t)M * G);              // [M][G] C of the group
-  const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
   const int nw = blockDim.x >> 6;

@@ -54,7 +54,6 @@ __global__ __launch_bounds__(1024) void k_dense_chunk(DenseArgs a) {
   head_stage_init(hst);  // ordered by the barriers below
   float* scores = reinterpret_cast<float*>(dyn_lds);  // [M][C]
   const int C = a.chunk_rows;
-  const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
   const int esz = BF16 ? 2 : 4;

@@ -304,7 +304,6 @@ template <int R, typename Sink>
 __device__ uint32_t block_compact(const uint32_t (&key)[R], uint32_t valid, const SelectRange& s,
                                   const uint32_t (&vbits)[R], const int32_t (&index)[R],
                                   SelectSmem& sm, Sink&& sink) {
-  const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
   const int nw = blockDim.x >> 6;
