@@ -87,8 +87,21 @@ def _select(**kw):
                                  a["indices"], a["ws"], a["ws_bytes"], a["opt"], a["stream"])
 
 
-def opt(chunk_rows=0, reserved=0):
-    return ctypes.byref(lt._Options(chunk_rows, reserved, None))
+def opt(chunk_rows=0, reserved=0, lse=None, allowed=None):
+    return ctypes.byref(lt._Options(chunk_rows, reserved, None, lse, allowed))
+
+
+def test_options_layout_matches_the_header():
+    # chunk_rows, reserved (int32 each), then three pointers: score_events, lse, allowed
+    assert ctypes.sizeof(lt._Options) == 8 + 3 * ctypes.sizeof(ctypes.c_void_p)
+    assert lt._Options.lse.offset == 16 and lt._Options.allowed.offset == 24
+
+
+@pytest.mark.parametrize("entry", ["binary", "dense", "select"])
+def test_misaligned_lse_or_bitmask_is_rejected_before_any_launch(entry):
+    call = {"binary": _binary, "dense": _dense, "select": _select}[entry]
+    assert call(opt=opt(lse=ODD)) == ALIGN
+    assert call(opt=opt(allowed=ODD)) == ALIGN
 
 
 @pytest.mark.parametrize("kw,code", [
