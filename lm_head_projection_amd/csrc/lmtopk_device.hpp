@@ -396,11 +396,11 @@ __device__ __forceinline__ void head_stage_init(HeadStage& st) {
 //           entry's position in (key desc, idx asc) order;
 //   else:   rank[i] += #{j : key[j] >= key[i]} (idx unused; the entry itself
 //           counts).
-// Wave w takes the slices of 16 entries j = w, w + nw, ... (each read as
-// four LDS broadcasts per array) against every block of 64 entries i, and
-// adds a slice's count with one LDS atomic per entry (integer adds: the
-// result does not depend on their order).  Few wide slices keep the
-// per-slice overhead small; the whole workgroup's VALU is one shared pool.
+// The jobs (slice of 16 entries j, read as four LDS broadcasts per array;
+// block of 64 entries i) are spread over every wave, and each adds its
+// counts with one LDS atomic per entry (integer adds: the result does not
+// depend on their order).  Wide slices keep the per-job overhead small; the
+// whole workgroup's VALU is one shared pool.
 // key and idx must be readable up to index 16 * ceil(n / 16) (entries past
 // n are not counted); rank[0, n) must be zero on entry; the caller orders
 // the result with a barrier.
@@ -413,7 +413,9 @@ __device__ __forceinline__ void rank_count(const uint32_t* key, const int32_t* i
   const uint32_t wave = (uint32_t)wave_id(), nw = blockDim.x >> 6;
   const uint32_t nb = (n + 63u) >> 6;
   const uint32_t ns = (n + 15u) >> 4;
-  for (uint32_t sl = wave; sl < ns; sl += nw) {
+  // job = (slice, block), spread over every wave
+  for (uint32_t job = wave; job < ns * nb; job += nw) {
+    const uint32_t sl = job % ns, b = job / ns;
     const uint32_t j0 = sl * 16u;
     uint32_t kj[16];
     int32_t ij[16];
@@ -435,19 +437,17 @@ __device__ __forceinline__ void rank_count(const uint32_t* key, const int32_t* i
       }
     }
     const uint32_t m = min(16u, n - j0);  // real entries in this slice
-    for (uint32_t b = 0; b < nb; ++b) {
-      const uint32_t i = b * 64u + (uint32_t)lane;
-      const bool vi = i < n;
-      const uint32_t ki = vi ? key[i] : 0u;
-      const int32_t ii = (kAhead && vi) ? (idx ? idx[i] : (int32_t)i) : 0;
-      uint32_t c = 0u;
+    const uint32_t i = b * 64u + (uint32_t)lane;
+    const bool vi = i < n;
+    const uint32_t ki = vi ? key[i] : 0u;
+    const int32_t ii = (kAhead && vi) ? (idx ? idx[i] : (int32_t)i) : 0;
+    uint32_t c = 0u;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const bool hit = kAhead ? (kj[e] > ki || (kj[e] == ki && ij[e] < ii)) : kj[e] >= ki;
-        c += ((uint32_t)e < m && hit) ? 1u : 0u;
-      }
-      if (vi && c) atomicAdd(&rank[i], c);
+    for (int e = 0; e < 16; ++e) {
+      const bool hit = kAhead ? (kj[e] > ki || (kj[e] == ki && ij[e] < ii)) : kj[e] >= ki;
+      c += ((uint32_t)e < m && hit) ? 1u : 0u;
     }
+    if (vi && c) atomicAdd(&rank[i], c);
   }
 }
 
