@@ -21,17 +21,28 @@ Modules
   normalizer  -- log-sum-exp of each row (the normalizer of the top-k
                  log-probabilities).
   mask        -- a grammar bitmask applied to logits (disallowed -> -inf).
+  sample      -- one token drawn from the top-k survivors: temperature, the
+                 top-k / top-p / min-p keep set, a Gumbel-max draw from a
+                 Philox4x32-10 counter-based generator.
 """
 
 from .projection import (
     bf16_bits_to_f32,
-    dequantize_binary,
     project_binary,
     project_dense,
 )
 from .select import certify_topk, float_key_order, topk_stable, topk_stable_rows
 from .normalizer import logsumexp_row, logsumexp_rows
 from .mask import allowed_bool, apply_allowed
+from .sample import (
+    draw_uniform,
+    gumbel,
+    keep_count,
+    philox4x32_10,
+    sample_row,
+    sample_rows,
+    uniform_from_word,
+)
 from .packing import (
     pack_layout_bytes,
     pack_logical,
@@ -41,7 +52,6 @@ from .packing import (
 
 __all__ = [
     "bf16_bits_to_f32",
-    "dequantize_binary",
     "project_binary",
     "project_dense",
     "certify_topk",
@@ -56,4 +66,11 @@ __all__ = [
     "pack_logical",
     "packed_sizes",
     "unpack_layout_bytes",
+    "philox4x32_10",
+    "uniform_from_word",
+    "draw_uniform",
+    "gumbel",
+    "keep_count",
+    "sample_row",
+    "sample_rows",
 ]

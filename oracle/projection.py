@@ -42,20 +42,6 @@ def project_dense(hidden, weight, bias=None, block_rows=4096):
     return out
 
 
-def dequantize_binary(signs, scales):
-    """Dequantized binary weights: sign[v, j] * scale[v, j // 128], float64.
-
-    lm-head-topk page, section "Usage": a binary head is a matrix of signs
-    with one scale per group of group_size=128 consecutive weights of a row.
-    signs: [V, H] with entries +1 / -1; scales: [V, H // 128] fp32.
-    """
-    s = np.asarray(signs, dtype=np.float64)
-    sc = np.asarray(scales, dtype=np.float64)
-    V, H = s.shape
-    assert H % GROUP == 0 and sc.shape == (V, H // GROUP)
-    return s * np.repeat(sc, GROUP, axis=1)
-
-
 def project_binary(act_q, act_scale, signs, scales, bias=None, block_rows=4096):
     """Binary head logits, the "dequantized reference" of the lm-head-topk page.
 

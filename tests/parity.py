@@ -20,11 +20,17 @@ terms of total magnitude mag: n * 2^-24 * mag, with n and mag given by the
 caller for its accumulation order.
 """
 
+import os
+
 import numpy as np
 
 import oracle
 
 U = 2.0 ** -24
+
+# (test id, row, position, gpu index, oracle index) of every relaxed
+# position, printed per test at the end of the session (tests/conftest.py)
+RELAXED = []
 
 
 def assert_select_exact(logits, vals, idx, k):
@@ -44,7 +50,9 @@ def compare_end_to_end(L, vals, idx, k, rtol, eps_fn, floor_rel=1e-3):
 
     eps_fn(m, indices) -> array of fp32 error bounds for those entries.
     Returns the number of positions where the GPU order differs from the
-    oracle's within the rounding allowance (informational).
+    oracle's within the rounding allowance; each one is also recorded in
+    RELAXED under the running test's name and reported at the end of the
+    session.  Any other difference fails.
     """
     L = np.asarray(L, dtype=np.float64)
     M, V = L.shape
@@ -80,6 +88,8 @@ def compare_end_to_end(L, vals, idx, k, rtol, eps_fn, floor_rel=1e-3):
                 assert abs(ref[i] - ov[i]) <= tol, \
                     f"row {m} pos {i}: gpu idx {gi[i]} (L={ref[i]!r}) vs oracle {oi[i]} (L={ov[i]!r})"
                 relaxed += 1
+                test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+                RELAXED.append((test, m, i, int(gi[i]), int(oi[i])))
     return relaxed
 
 

@@ -401,3 +401,204 @@ def test_mask_all_and_none_and_independent_packing():
     bm = np.packbits(padded, axis=1, bitorder="little").view("<i4")
     assert np.array_equal(oracle.allowed_bool(bm, V), want)
     assert np.array_equal(oracle.apply_allowed(L, bm), np.where(want, L, -np.inf).astype(np.float32))
+
+
+def test_topk_stable_rows_brute_force_and_dtype():
+    """Each row's (values, indices) equal the brute-force ranking of that row,
+    and the values keep the input's dtype and bits."""
+    rng = np.random.default_rng(22)
+    for dtype in (np.float32, np.float64):
+        L = np.floor(rng.normal(size=(5, 40)) * 3).astype(dtype)
+        L[1, 3] = -0.0
+        L[2, :] = 1.0
+        for k in (1, 7, 40):
+            vals, idx = oracle.topk_stable_rows(L, k)
+            assert vals.dtype == dtype and idx.dtype == np.int64
+            assert vals.shape == (5, k) and idx.shape == (5, k)
+            for m in range(5):
+                ranks = rank_by_counting(L[m].tolist())
+                want = sorted(range(40), key=lambda i: ranks[i])[:k]
+                assert idx[m].tolist() == want
+                assert np.array_equal(vals[m].view(np.uint8), L[m, want].view(np.uint8))
+
+
+# ---------------------------------------------------------------------------
+# sampling over the survivors (logits-processor page, sections "API" and
+# "Method": temperature, top-k / top-p / min-p keep set, Gumbel-max draw
+# keyed by (seed, row, offset))
+# ---------------------------------------------------------------------------
+def test_philox_known_answer_vectors():
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        ctr = [int(x, 16) for x in case["counter"]]
+        key = [int(x, 16) for x in case["key"]]
+        want = tuple(int(x, 16) for x in case["out"])
+        assert oracle.philox4x32_10(ctr, key) == want
+
+
+def test_uniform_and_gumbel_closed_forms():
+    # u = (x >> 9 + 1/2) * 2^-23: ends of the range, and every value fits fp32
+    assert oracle.uniform_from_word(0) == 2.0 ** -24
+    assert oracle.uniform_from_word(0xFFFFFFFF) == 1.0 - 2.0 ** -24
+    assert oracle.uniform_from_word(1 << 31) == 0.5 + 2.0 ** -24
+    assert oracle.uniform_from_word(511) == oracle.uniform_from_word(0)  # low 9 bits dropped
+    for x in (0, 12345, 1 << 31, 0xFFFFFFFF, 0xDEADBEEF):
+        u = oracle.uniform_from_word(x)
+        assert float(np.float32(u)) == u and 0.0 < u < 1.0
+    # the Gumbel inverse CDF: F(x) = exp(-exp(-x)), so gumbel(F(x)) = x
+    for x in (-2.0, 0.0, 0.5, 3.0, 10.0):
+        assert math.isclose(oracle.gumbel(math.exp(-math.exp(-x))), x, rel_tol=1e-12, abs_tol=1e-12)
+    # larger u, larger noise
+    us = [oracle.uniform_from_word(x) for x in (0, 1 << 20, 1 << 30, 3 << 30, 0xFFFFFFFF)]
+    gs = [oracle.gumbel(u) for u in us]
+    assert all(a < b for a, b in zip(gs, gs[1:]))
+
+
+def test_draw_keying():
+    """The uniform depends on every part of the key (seed, row, offset incl.
+    its high word, vocabulary entry) and nothing else."""
+    base = oracle.draw_uniform(7, 2, 5, 1000)
+    assert oracle.draw_uniform(7, 2, 5, 1000) == base
+    others = [oracle.draw_uniform(8, 2, 5, 1000), oracle.draw_uniform(7, 3, 5, 1000),
+              oracle.draw_uniform(7, 2, 6, 1000), oracle.draw_uniform(7, 2, 5, 1001),
+              oracle.draw_uniform(7, 2, 5 + (1 << 32), 1000), oracle.draw_uniform(7 + (1 << 32), 2, 5, 1000)]
+    assert all(u != base for u in others)
+    # the word it uses is the first output of the generator at that counter and key
+    x = oracle.philox4x32_10((1000, 2, 5, 0), (7, 0))[0]
+    assert base == oracle.uniform_from_word(x)
+
+
+def test_keep_count_hand_worked():
+    # probabilities 1/2, 1/4, 1/8, 1/8 over the whole vocabulary (lse = 0)
+    z = np.log(np.array([0.5, 0.25, 0.125, 0.125]))
+    kc = oracle.keep_count
+    assert kc(z, 0.0, 0, 1.0, 0.0) == 4          # every filter off
+    assert kc(z, 0.0, 3, 1.0, 0.0) == 3          # top-k
+    assert kc(z, 0.0, 10, 1.0, 0.0) == 4         # top_k beyond k: k
+    assert kc(z, 0.0, 0, 0.49, 0.0) == 1         # mass before position 1 is 1/2
+    assert kc(z, 0.0, 0, 0.74, 0.0) == 2         # 3/4 before position 2
+    assert kc(z, 0.0, 0, 0.76, 0.0) == 3         # 7/8 before position 3
+    assert kc(z, 0.0, 0, 0.9, 0.0) == 4
+    assert kc(z, 0.0, 0, 1.0, 0.3) == 2          # ratios 1, 1/2, 1/4, 1/4
+    assert kc(z, 0.0, 0, 1.0, 0.2) == 4
+    assert kc(z, 0.0, 3, 0.9, 0.2) == 3          # the intersection is the shortest prefix
+    assert kc(z, 0.0, 0, 0.76, 0.3) == 2
+    assert kc(np.array([0.0, -np.inf, -np.inf]), 0.0, 0, 1.0, 0.0) == 1
+    # a normalizer over a larger vocabulary scales the probabilities down
+    # probabilities 1/4, 1/8, 1/16, 1/16: masses before positions 1..3 are
+    # 1/4, 3/8, 7/16
+    assert kc(z, math.log(2.0), 0, 0.4, 0.0) == 3
+    assert kc(z, math.log(2.0), 0, 0.45, 0.0) == 4
+
+
+def _cutoff_keep(p_full, k, top_k, top_p, min_p):
+    """The filters as one probability cutoff over the whole vocabulary (the
+    logits-processor page's formulation), for distinct probabilities: the
+    number of tokens whose probability is at least every filter's cutoff,
+    then limited to the k survivors."""
+    p = np.sort(np.asarray(p_full))[::-1]
+    cuts = [0.0]
+    if top_k > 0:
+        cuts.append(p[min(top_k, len(p)) - 1])
+    if top_p < 1.0:
+        csum = np.cumsum(p)
+        n = int(np.searchsorted(csum, top_p, side="left")) + 1  # first n with mass >= top_p
+        cuts.append(p[min(n, len(p)) - 1])
+    if min_p > 0.0:
+        cuts.append(min_p * p[0])
+    return min(int(np.sum(p >= max(cuts))), k)
+
+
+def test_keep_count_equals_single_cutoff():
+    rng = np.random.default_rng(23)
+    for trial in range(300):
+        V = int(rng.integers(2, 40))
+        L = rng.normal(0.0, 2.0, size=V)
+        T = float(rng.choice([0.5, 1.0, 1.7]))
+        k = int(rng.integers(1, V + 1))
+        top_k = int(rng.choice([0, 1, 3, 8, 100]))
+        top_p = float(rng.choice([1.0, 0.3, 0.8, 0.95]))
+        min_p = float(rng.choice([0.0, 0.05, 0.3]))
+        zf = L / T
+        lse = oracle.logsumexp_row(zf)
+        p_full = np.exp(zf - lse)
+        vals, idx = oracle.topk_stable(L, k)
+        got = oracle.keep_count(vals / T, lse, top_k, top_p, min_p)
+        want = _cutoff_keep(p_full, k, top_k, top_p, min_p)
+        # the cumulative sums are only float64-exact: skip draws within rounding of a cut
+        csum = np.cumsum(np.sort(p_full)[::-1])
+        if np.min(np.abs(csum - top_p)) < 1e-12 or np.min(np.abs(p_full / p_full.max() - min_p)) < 1e-12:
+            continue
+        assert got == max(1, want), (trial, got, want)
+
+
+def test_sample_greedy_cases():
+    rng = np.random.default_rng(24)
+    L = rng.normal(size=(3, 50))
+    L[1, 7] = L[1, 30] = L[1].max() + 1.0  # tie for the maximum: lower index
+    first_max = [int(np.argmax(L[m])) for m in range(3)]
+    for kw in ({"temperature": 0.0}, {"temperature": -1.0}, {"top_k": 1}, {"top_p": 0.0}):
+        for k in (1, 5, 50):
+            args = dict(temperature=0.8, top_k=0, top_p=1.0, min_p=0.0, seed=3, offset=9)
+            args.update(kw)
+            tokens, kept = oracle.sample_rows(L, k, **args)
+            assert tokens.tolist() == first_max and kept.tolist() == [1, 1, 1]
+    # min_p = 1 keeps exactly the entries equal to the maximum (both tied ones in row 1)
+    tokens, kept = oracle.sample_rows(L, 50, temperature=0.8, min_p=1.0, seed=3, offset=9)
+    assert kept.tolist() == [1, 2, 1] and tokens[1] in (7, 30)
+    assert tokens[0] == first_max[0] and tokens[2] == first_max[2]
+    # k = 1 whatever the parameters
+    tokens, kept = oracle.sample_rows(L, 1, temperature=2.0, top_p=1.0, seed=1, offset=2)
+    assert tokens.tolist() == first_max and kept.tolist() == [1, 1, 1]
+    # an +inf logit wins outright; an all -inf row returns its first index
+    Li = np.array([[0.0, np.inf, 1.0, np.inf], [-np.inf] * 4])
+    tokens, kept = oracle.sample_rows(Li, 3, temperature=1.0, seed=0, offset=0)
+    assert tokens.tolist() == [1, 0] and kept.tolist() == [1, 1]
+
+
+def test_gumbel_max_matches_the_filtered_softmax():
+    """20,000 draws (offsets 0..19,999) land in the keep set only, with the
+    frequencies of the renormalized softmax over it (chi-square, p < 1e-6
+    would fail): a wrong sign or scale of the noise, or of the temperature,
+    fails this."""
+    scipy_stats = pytest.importorskip("scipy.stats")
+    L = np.array([[2.0, 1.2, 1.0, 0.3, -0.5, -1.0, -3.0, 0.9]])
+    T, top_p, min_p, k = 0.8, 0.9, 0.05, 6
+    r = oracle.sample_row(L[0], k, T, 0, top_p, min_p, seed=11, row=0, offset=0)
+    n = r["kept"]
+    keep_idx = r["indices"][:n].tolist()
+    assert 2 <= n < k  # the filters bite in this case
+    w = np.exp(r["z"][:n] - r["z"][0])
+    expect = w / w.sum()
+    draws = 20000
+    counts = dict.fromkeys(keep_idx, 0)
+    for off in range(draws):
+        tok = oracle.sample_row(L[0], k, T, 0, top_p, min_p, seed=11, row=0, offset=off)["token"]
+        assert tok in counts
+        counts[tok] += 1
+    obs = np.array([counts[i] for i in keep_idx], dtype=np.float64)
+    stat = float(np.sum((obs - draws * expect) ** 2 / (draws * expect)))
+    assert stat < scipy_stats.chi2.ppf(1.0 - 1e-6, n - 1), (stat, obs, draws * expect)
+
+
+def test_sample_rows_per_row_parameters():
+    rng = np.random.default_rng(25)
+    M, V, k = 4, 300, 40
+    L = rng.normal(size=(M, V))
+    T = np.array([0.0, 0.5, 1.0, 2.0])
+    tk = np.array([0, 5, 40, 3])
+    tp = np.array([1.0, 0.9, 0.5, 1.0])
+    mp = np.array([0.0, 0.0, 0.1, 0.5])
+    tokens, kept = oracle.sample_rows(L, k, T, tk, tp, mp, seed=5, offset=77)
+    for m in range(M):
+        r = oracle.sample_row(L[m], k, T[m], tk[m], tp[m], mp[m], seed=5, row=m, offset=77)
+        assert tokens[m] == r["token"] and kept[m] == r["kept"]
+    assert kept[0] == 1 and kept[3] <= 3
+    # the row is part of the key: equal rows draw differently at some offset
+    L2 = np.repeat(L[:1], 2, axis=0)
+    diff = 0
+    for off in range(20):
+        t2, _ = oracle.sample_rows(L2, k, 1.0, 0, 1.0, 0.0, seed=5, offset=off)
+        diff += int(t2[0] != t2[1])
+    assert diff > 0
