@@ -18,16 +18,19 @@
  *    no memory; the caller owns every buffer, including outputs and workspace.
  *    Inputs are read only; outputs are fully overwritten on success.
  *  - Arrays are dense and row-major.  Every pointer must be 16-byte aligned.
- *  - Arguments are checked on the host BEFORE anything is enqueued.  On any
- *    error status nothing is launched and nothing is written.  A failure
- *    reported by the HIP runtime while enqueueing maps to LMTOPK_ERR_HIP; a
- *    fault inside a kernel surfaces at the caller's next synchronisation, as
- *    for any asynchronous HIP work.
- *  - The library keeps no state of its own and is thread safe.  A workspace
- *    must be zero-filled once before its first use (e.g. hipMemset after
- *    hipMalloc); every call leaves its first 256 bytes zero again when it
- *    completes and overwrites whatever else it reads.  Calls that share a
- *    workspace must be ordered on one stream.
+ *  - Arguments are checked on the host BEFORE anything is enqueued.  The only
+ *    HIP calls made before that are read-only queries of the current device
+ *    (its LDS limit per workgroup).  On any error status nothing is launched
+ *    and nothing is written.  A failure reported by the HIP runtime while
+ *    enqueueing maps to LMTOPK_ERR_HIP; a fault inside a kernel surfaces at
+ *    the caller's next synchronisation, as for any asynchronous HIP work.
+ *  - The library keeps no state of its own and is thread safe.  The caller's
+ *    workspace carries one thing from call to call: a completion counter in
+ *    its first 256 bytes, which must be zero before a call starts.  Prepare a
+ *    new workspace once with lmtopk_workspace_init (or any zero fill); every
+ *    call leaves the counter zero again when it completes and overwrites
+ *    whatever else it reads.  Calls that share a workspace must be ordered on
+ *    one stream; calls that overlap in time need workspaces of their own.
  *  - Inputs must be finite or +-inf.  NaN anywhere is outside the contract and
  *    gives an unspecified (but memory-safe) result.
  *  - +0.0 and -0.0 compare equal: they tie and the lower index comes first.
@@ -71,8 +74,9 @@ typedef enum { LMTOPK_F32 = 0, LMTOPK_BF16 = 1 } lmtopk_dtype;
 /* Optional per-call settings; pass NULL for the defaults. */
 typedef struct {
   /* Vocabulary rows per chunk (one workgroup scores and selects one chunk).
-     0 = automatic.  Otherwise a multiple of 64 that is <= 1024, or 2048.
-     The result never depends on this value. */
+     0 = automatic.  Otherwise a multiple of 64 that is <= 1024, or 2048
+     (lmtopk_binary: 2048 only for M <= 2, OPTIONS otherwise).  The result
+     never depends on this value. */
   int32_t chunk_rows;
   int32_t reserved; /* must be 0 */
   /* If not NULL: the address of two hipEvent_t (an array void*[2]).  The
@@ -98,7 +102,62 @@ typedef struct {
      when fewer than k entries are allowed, after every allowed one, in index
      order.  Bits past V are ignored.  16-byte aligned. */
   const int32_t* allowed;
+  /* If not NULL: draw one token per row from the call's top-k survivors
+     (lmtopk_sampling below).  A host pointer, read during the call. */
+  const struct lmtopk_sampling* sampling;
 } lmtopk_options;
+
+/*
+ * Sampling one token per row from the top-k survivors (logits-processor
+ * page, section "API": sample(logits, temperature, top_k, top_p, min_p,
+ * seed, offset); section "Method": the three filters meet in one keep set
+ * and the token is drawn by Gumbel-max over it).  The draw is fused after
+ * the exact top-k, so it sees the call's k survivors in output order
+ * (value descending, lower index first) and never a token outside them.
+ * For row m, with T its temperature, z_i = values[m, i] * (1 / T) in fp32
+ * and lse_T = log sum over all V entries of exp(L[m, v] / T) (the whole
+ * vocabulary; disallowed entries of a bitmask count as -inf):
+ *   - the keep set is a prefix of the survivors: position 0 always; position
+ *     i >= 1 while every earlier one was kept and
+ *       i < top_k                       (top_k <= 0 or >= k: any i < k),
+ *       p_0 + ... + p_{i-1} < top_p,   p_j = exp(z_j - lse_T)   (top_p < 1),
+ *       exp(z_i - z_0) >= min_p                                 (min_p > 0),
+ *       z_i > -inf;
+ *   - the token is the index of the kept position with the largest
+ *     z_i + g_i, g_i = -log(-log(u_i)), the lower position on a tie; u_i is
+ *     the uniform of Philox4x32-10 (Salmon et al., SC 2011) at key (seed mod
+ *     2^32, seed div 2^32) and counter (vocabulary index, m, offset mod 2^32,
+ *     offset div 2^32): its first output word x, u = (x >> 9) * 2^-23 +
+ *     2^-24;
+ *   - temperature <= 0 is greedy: the token is indices[m, 0] (the argmax,
+ *     lower index on ties), keep-set size 1; likewise when values[m, 0] is
+ *     +inf or every logit of the row is -inf.
+ * With sampling, lmtopk_options.lse (if given) receives lse_T, the
+ * normaliser of the distribution sampled from (log-sum-exp of L / T; of L
+ * itself for greedy rows).  Each parameter applies to every row unless its
+ * per-row device array is given.  Cost: the survivors' k values are already
+ * on chip; top-p (any row with top_p < 1, or top_p_rows given) adds the
+ * per-chunk normaliser partials of the lse option.
+ */
+typedef struct lmtopk_sampling {
+  float temperature;               /* <= 0: greedy                          */
+  int32_t top_k;                   /* <= 0: off; must be <= k (else OPTIONS) */
+  float top_p;                     /* >= 1: off                             */
+  float min_p;                     /* <= 0: off                             */
+  const float* temperature_rows;   /* [M] device, or NULL                   */
+  const int32_t* top_k_rows;       /* [M] device, or NULL (a value above k
+                                      or <= 0 means k)                      */
+  const float* top_p_rows;         /* [M] device, or NULL                   */
+  const float* min_p_rows;         /* [M] device, or NULL                   */
+  uint64_t seed;
+  uint64_t offset;                 /* advance it every decoding step        */
+  const uint64_t* offset_device;   /* [1] device, or NULL: if given, the
+                                      offset is read from it when the call
+                                      runs (a captured graph can then be
+                                      replayed with a new offset)           */
+  int64_t* tokens;                 /* out [M] device                        */
+  int32_t* kept;                   /* out [M] device, or NULL: keep-set size */
+} lmtopk_sampling;
 
 /* ------------------------------------------------------------------------ */
 /* Packed binary head, layout version 1                                      */
@@ -164,6 +223,13 @@ lmtopk_status lmtopk_packed_bytes(int64_t V, int64_t H, int32_t group_size,
 lmtopk_status lmtopk_workspace_bytes(int64_t M, int64_t V, int32_t k,
                                      const lmtopk_options* opt, size_t* bytes);
 
+/* Zero-fill a workspace of `bytes` bytes (device pointer, 16-byte aligned)
+   on `stream`, with a kernel rather than a memset so that the call may be
+   captured into a graph.  Needed once per new workspace (see the
+   conventions above); calls leave it ready for the next call.
+   Errors: NULL, ALIGN, HIP. */
+lmtopk_status lmtopk_workspace_init(void* workspace, size_t bytes, void* stream);
+
 /*
  * Pack a dense head into the layout above (offline; once per model).
  *   w      : [V, H] row-major, fp32 or bf16 (w_dtype).
@@ -192,7 +258,7 @@ lmtopk_status lmtopk_pack_binary(const void* w, lmtopk_dtype w_dtype, int64_t V,
  *         (float)D_g * wscale[v, g], starting from 0
  *   L   = fmaf(acc, act_scale[m], bias ? bias[v] : 0)
  * Errors: NULL, SHAPE (also M * H > LMTOPK_MAX_BINARY_MH), K, GROUP, ALIGN,
- * WORKSPACE, OPTIONS, HIP.
+ * WORKSPACE, OPTIONS (also chunk_rows 2048 with M > 2), HIP.
  */
 lmtopk_status lmtopk_binary(const int8_t* act_q, const float* act_scale,
                             const void* wq, const float* wscale,
@@ -222,9 +288,14 @@ lmtopk_status lmtopk_dense(const void* hidden, const void* weight,
 
 /*
  * Selection stage alone on logits already in device memory: the exact top-k
- * of logits[m, 0:V] for each row (row stride ld >= V elements).  Same chunked
- * select and merge kernels as the fused paths, so the chunk select and merge
- * can be checked bit for bit against a plain sort.
+ * of logits[m, 0:V] for each row (row stride ld >= V elements).  This is the
+ * lm-head-topk page's second half on its own (section "Method": each chunk
+ * offers its top-k, a merge reduces them), applied to materialized logits,
+ * the form its section "Correctness" compares against (torch.topk on the
+ * materialized logits).  Same chunked select and merge kernels as the fused
+ * paths, so the chunk select and merge can be checked bit for bit against a
+ * plain sort; with lmtopk_options.sampling it is also the logits-processor
+ * page's sample() restricted to the top-k.
  * Errors: NULL, SHAPE, K, ALIGN, WORKSPACE, OPTIONS, HIP.
  */
 lmtopk_status lmtopk_select(const float* logits, int64_t M, int64_t V,

@@ -1,7 +1,8 @@
 // lmtopk_api.cpp - the C ABI of liblmtopk: argument checks, chunk geometry,
 // merge plan, and dispatch to the HIP launchers.  Plain host C++: every check
-// here runs before the first HIP call, so an invalid call launches nothing and
-// writes nothing.
+// here runs before anything is enqueued (the only HIP calls before that query
+// the device's LDS limit), so an invalid call launches nothing and writes
+// nothing.
 
 #include <stdint.h>
 #include <string.h>
@@ -157,6 +158,13 @@ lmtopk_status lmtopk_workspace_bytes(int64_t M, int64_t V, int32_t k, const lmto
   return LMTOPK_OK;
 }
 
+lmtopk_status lmtopk_workspace_init(void* workspace, size_t bytes, void* stream) {
+  if (!workspace) return LMTOPK_ERR_NULL;
+  if (!lmtopk::aligned16(workspace)) return LMTOPK_ERR_ALIGN;
+  if (bytes == 0) return LMTOPK_OK;
+  return lmtopk::hip_status(lmtopk::launch_zero(workspace, bytes, stream));
+}
+
 lmtopk_status lmtopk_pack_binary(const void* w, lmtopk_dtype w_dtype, int64_t V, int64_t H,
                                  int32_t group_size, void* wq, float* wscale, void* stream) {
   if (!w || !wq || !wscale) return LMTOPK_ERR_NULL;
@@ -167,6 +175,36 @@ lmtopk_status lmtopk_pack_binary(const void* w, lmtopk_dtype w_dtype, int64_t V,
     return LMTOPK_ERR_ALIGN;
   return lmtopk::hip_status(
       lmtopk::launch_pack(w, w_dtype == LMTOPK_BF16, V, H, wq, wscale, stream));
+}
+
+// The call's token draw (lmtopk_sampling) into g->smp; OPTIONS for a scalar
+// top_k above k, NULL / ALIGN for the arrays.
+static lmtopk_status sampling_checks(const lmtopk_sampling* sp, int32_t k, Geometry* g) {
+  memset(&g->smp, 0, sizeof(g->smp));
+  if (!sp) return LMTOPK_OK;
+  if (!sp->tokens) return LMTOPK_ERR_NULL;
+  if (sp->top_k > k) return LMTOPK_ERR_OPTIONS;
+  const void* arrays[] = {sp->tokens, sp->kept, sp->temperature_rows, sp->top_k_rows,
+                          sp->top_p_rows, sp->min_p_rows, sp->offset_device};
+  for (const void* p : arrays)
+    if (p && !lmtopk::aligned16(p)) return LMTOPK_ERR_ALIGN;
+  lmtopk::SampleParams& s = g->smp;
+  s.on = 1;
+  s.need_norm = (sp->top_p_rows != nullptr || sp->top_p < 1.f) ? 1 : 0;
+  s.temperature = sp->temperature;
+  s.top_k = sp->top_k;
+  s.top_p = sp->top_p;
+  s.min_p = sp->min_p;
+  s.temperature_rows = sp->temperature_rows;
+  s.top_k_rows = sp->top_k_rows;
+  s.top_p_rows = sp->top_p_rows;
+  s.min_p_rows = sp->min_p_rows;
+  s.seed = sp->seed;
+  s.offset = sp->offset;
+  s.offset_device = sp->offset_device;
+  s.tokens = sp->tokens;
+  s.kept = sp->kept;
+  return LMTOPK_OK;
 }
 
 static lmtopk_status common_checks(const void* workspace, size_t workspace_bytes, float* values,
@@ -182,6 +220,8 @@ static lmtopk_status common_checks(const void* workspace, size_t workspace_bytes
   if (g->lse && !lmtopk::aligned16(g->lse)) return LMTOPK_ERR_ALIGN;
   g->allowed = opt ? opt->allowed : nullptr;
   if (g->allowed && !lmtopk::aligned16(g->allowed)) return LMTOPK_ERR_ALIGN;
+  st = sampling_checks(opt ? opt->sampling : nullptr, k, g);
+  if (st) return (lmtopk_status)st;
   if (!workspace || workspace_bytes < g->workspace_bytes) return LMTOPK_ERR_WORKSPACE;
   if (!lmtopk::aligned16(workspace)) return LMTOPK_ERR_ALIGN;
   return LMTOPK_OK;
@@ -210,6 +250,7 @@ lmtopk_status lmtopk_binary(const int8_t* act_q, const float* act_scale, const v
   if (H < 1) return LMTOPK_ERR_SHAPE;
   if (group_size != LMTOPK_GROUP_SIZE || H % LMTOPK_GROUP_SIZE != 0) return LMTOPK_ERR_GROUP;
   if (M * H > LMTOPK_MAX_BINARY_MH) return LMTOPK_ERR_SHAPE;
+  if (g.rpl > 1 && M > lmtopk::kMaxRowsWide) return LMTOPK_ERR_OPTIONS;
   if (!lmtopk::aligned16(act_q) || !lmtopk::aligned16(act_scale) || !lmtopk::aligned16(wq) ||
       !lmtopk::aligned16(wscale) || (bias && !lmtopk::aligned16(bias)))
     return LMTOPK_ERR_ALIGN;

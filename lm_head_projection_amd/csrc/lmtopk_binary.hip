@@ -209,6 +209,8 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   // hold up the barrier below, which waits for every scalar load, by a full
   // memory round trip)
   const float act_sv = a.act_scale[lane < M ? lane : M - 1];
+  // lane m: row m's temperature (the draw's logit scale for the normaliser)
+  const float temp_v = kExtras ? row_temperature(a.out, lane < M ? lane : M - 1, a.act_scale) : 1.f;
   // the call's bitmask bits of this lane's rows, per activation row
   uint32_t allow[M];
   {
@@ -372,19 +374,23 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     float val[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) val[r] = fmaf(acc[r][m], s, bias_v[r]);
-    chunk_select_write<R, kExtras>(val, idx, valid, m, a.out, ssm, hst, m == M - 1, allow[m]);
+    const float zs = z_scale(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(temp_v), m)));
+    chunk_select_write<R, kExtras>(val, idx, valid, m, a.out, ssm, hst, m == M - 1, allow[m], zs);
   }
   if (a.out.fused) fused_merge_tail<kFusedRM, kExtras>(fused_merge_of(a.out), ssm, csm.fs, last_wg);
 }
 namespace {
 
-// kExtras: a log-sum-exp output or a bitmask (kernels without them leave
-// that code out)
+// kExtras: a log-sum-exp output, a bitmask or a token draw (kernels without
+// them leave that code out)
+// 2048-row chunks (4 rows per lane) exist for one and two rows only: from
+// three rows on their accumulators and weight buffers no longer fit the
+// registers (the host refuses that option there).
 template <int M>
 void (*binary_kernel_m(int rpl, bool extras))(BinaryArgs) {
-  switch (rpl) {
-    case 1: return extras ? k_binary_chunk<M, 1, true> : k_binary_chunk<M, 1, false>;
-    case 4: return extras ? k_binary_chunk<M, 4, true> : k_binary_chunk<M, 4, false>;
+  if (rpl == 1) return extras ? k_binary_chunk<M, 1, true> : k_binary_chunk<M, 1, false>;
+  if constexpr (M <= kMaxRowsWide) {
+    if (rpl == 4) return extras ? k_binary_chunk<M, 4, true> : k_binary_chunk<M, 4, false>;
   }
   return nullptr;
 }
@@ -425,7 +431,7 @@ int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* ac
   a.Q = (a.G + 3) / 4;
   a.tiles_per_chunk = g.chunk_rows / 64;
   a.out = chunk_out(g, workspace, values, indices);
-  auto kern = binary_kernel((int)g.M, g.rpl, g.lse != nullptr || g.allowed != nullptr);
+  auto kern = binary_kernel((int)g.M, g.rpl, g.lse != nullptr || g.allowed != nullptr || g.smp.on);
   if (!kern) return (int)hipErrorInvalidValue;
   return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), binary_lds_bytes(g.M, H), stream, a,
                       events);

@@ -10,8 +10,83 @@
 
 #include "lmtopk_device.hpp"
 #include "lmtopk_internal.hpp"
+#include "lmtopk_sample.hpp"
 
 namespace lmtopk {
+
+// LDS of a chunk kernel: the chunk selection's staging, and, after it, the
+// final merge of the fused path.
+union ChunkSmem {
+  HeadStage hs;
+  FinalSmem fs;
+};
+
+// What the fused final merge needs: the launch's candidate lists and heads,
+// the outputs, and a workspace counter that is zero between calls.
+struct FusedMerge {
+  uint32_t* counter;
+  const uint2* cand;   // [M][n_chunks][kc]
+  const uint2* heads;  // [M][n_chunks][kHeads]
+  float* values;       // [M][k]
+  int64_t* indices;    // [M][k]
+  int M;
+  int n_chunks;
+  int kc;
+  int k;
+  const uint2* lse_part;  // [M][n_chunks][waves] (max, sum) pairs, or null
+  float* lse;             // [M] or null
+  SampleParams smp;       // the token draw (smp.on == 0: none)
+};
+
+// Fused second pass (lm-head-topk page, section "Method": the chunk
+// candidates are merged into the final top-k).  Called by every workgroup
+// of a chunk launch (one workgroup per chunk) after it has stored its
+// candidates and heads with st_cand.  Each workgroup waits until those
+// stores are complete at device scope, then counts itself done on the
+// counter; the workgroup that counts last sees every chunk's candidates and
+// merges all M rows, then sets the counter back to zero for the next call.
+// n_chunks * kc <= blockDim.x * RM.  With a token draw, each row's token is
+// drawn right after its merge (sample_row).
+// kExtras false: the launch has no log-sum-exp output, bitmask or draw, and
+// that code is left out.
+template <int RM, bool kExtras = true>
+__device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem& sm, FinalSmem& fs,
+                                 uint32_t& last) {
+  // every store of this thread has been acknowledged (gfx9 counts stores in vmcnt)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  if (threadIdx.x == 0) {
+    const uint32_t done =
+        __hip_atomic_fetch_add(f.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = done == (uint32_t)f.n_chunks - 1u ? 1u : 0u;
+  }
+  lds_barrier();
+  if (uniform(last) == 0u) return;
+  const int64_t n_in = (int64_t)f.n_chunks * f.kc;
+  const int n_part = f.n_chunks * (int)(blockDim.x >> 6);
+  for (int m = 0; m < f.M; ++m) {
+    // the row's log-sum-exp partials and draw parameters are requested
+    // before the merge, which waits for its own loads meanwhile
+    uint2 pre[kLsePairs];
+    bool have = false;
+    if (kExtras && f.lse_part != nullptr) have = load_lse_pairs(f.lse_part + (size_t)m * n_part, n_part, pre);
+    RowSample rs;
+    if (kExtras && f.smp.on) rs = load_row_sample(f.smp, m);
+    merge_final<RM>(f.cand + (size_t)m * n_in, n_in, f.heads + (size_t)m * f.n_chunks * kHeads,
+                    f.n_chunks, f.kc, (uint32_t)f.k, f.values + (size_t)m * f.k,
+                    f.indices + (size_t)m * f.k, (int)blockDim.x, sm, fs);
+    lds_barrier();  // fs.out_* are complete; fs is reused by the next row
+    float lse = 0.f;
+    if (kExtras && f.lse_part != nullptr)
+      lse = merge_lse(f.lse_part + (size_t)m * n_part, n_part, f.lse ? f.lse + m : nullptr, sm, have, pre);
+    if (kExtras && f.smp.on) {
+      sample_row(fs.out_bits, fs.out_idx, f.k, lse, rs, m, f.smp);
+      lds_barrier();  // fs is reused by the next row
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(f.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 
 struct ChunkOut {
   uint2* cand;        // [M][n_chunks][kc]
@@ -28,6 +103,7 @@ struct ChunkOut {
   float* lse;         // [M] or null
   const int32_t* allowed;  // bitmask [M][allowed_words] (bit 1 = allowed), or null
   int allowed_words;       // ceil(V / 32)
+  SampleParams smp;        // the token draw (smp.on == 0: none)
 };
 
 // The fused merge's view of a chunk launch's outputs.
@@ -44,6 +120,7 @@ __device__ __forceinline__ FusedMerge fused_merge_of(const ChunkOut& o) {
   f.k = o.k;
   f.lse_part = o.lse_part;
   f.lse = o.lse;
+  f.smp = o.smp;
   return f;
 }
 
@@ -80,13 +157,15 @@ __device__ __forceinline__ uint32_t allowed_bits(const ChunkOut& o, int m, const
 }
 
 // `allow` bit r clear: row r's logit counts as -inf (a disallowed entry).
-// kExtras false: the call has neither a log-sum-exp output nor a bitmask,
-// and that code is left out.
+// zs: the row's logits are scaled by zs before the normaliser partials (1 /
+// T of a sampled row, else 1); the candidates keep the logits themselves.
+// kExtras false: the call has no log-sum-exp output, bitmask or draw, and
+// that code is left out.
 template <int RPL, bool kExtras = true>
 __device__ __forceinline__ void chunk_select_write(const float (&val_in)[RPL], const int32_t (&idx)[RPL],
                                                    uint32_t valid, int m, const ChunkOut& o,
                                                    SelectSmem& sm, HeadStage& st, bool last,
-                                                   uint32_t allow = 0xFFFFFFFFu) {
+                                                   uint32_t allow = 0xFFFFFFFFu, float zs = 1.f) {
   float val[RPL];
   uint32_t key[RPL], vb[RPL];
 #pragma unroll
@@ -99,16 +178,19 @@ __device__ __forceinline__ void chunk_select_write(const float (&val_in)[RPL], c
   if (kExtras && o.lse_part != nullptr) {
     // this wave's (max, sum of exp(logit - max)) over its valid rows
     const int wave = wave_id();
+    float z[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) z[r] = val[r] * zs;
     float mx = -INFINITY;
 #pragma unroll
     for (int r = 0; r < RPL; ++r)
-      if ((valid >> r) & 1u) mx = fmaxf(mx, val[r]);
+      if ((valid >> r) & 1u) mx = fmaxf(mx, z[r]);
     mx = wave_max_f32(mx);
     float sum = mx == INFINITY ? 1.f : 0.f;
     if (mx != INFINITY && mx != -INFINITY) {
 #pragma unroll
       for (int r = 0; r < RPL; ++r)
-        if ((valid >> r) & 1u) sum += expf(val[r] - mx);
+        if ((valid >> r) & 1u) sum += expf(z[r] - mx);
     }
     sum = wave_sum_f32(sum);
     if (lane_id() == 0)
@@ -144,6 +226,17 @@ __device__ __forceinline__ void chunk_select_write(const float (&val_in)[RPL], c
   // a k < 4 is still a real logit of the row, which the merge may consider)
   block_heads<RPL>(key, valid, vb, idx, st, heads);
   if (!last) lds_barrier();  // the staging is refilled by the next row
+}
+
+// Row m's temperature (1 without a draw; its z_scale is what the normaliser
+// partials scale the logits by).  The load is unconditional, from `dummy`
+// (any valid address) when the temperatures do not come per row, so a
+// caller may issue it among loads whose count must not vary; the value is
+// read after the caller's main loop.
+__device__ __forceinline__ float row_temperature(const ChunkOut& o, int m, const float* dummy) {
+  const bool rows = o.smp.on && o.smp.temperature_rows != nullptr;
+  const float x = rows ? o.smp.temperature_rows[m] : *dummy;
+  return !o.smp.on ? 1.f : rows ? x : o.smp.temperature;
 }
 
 // Streaming loads of the head (and of logits on the selection-only path):
@@ -196,9 +289,11 @@ inline ChunkOut chunk_out(const Geometry& g, void* workspace, float* values, int
   o.lse = g.lse;
   o.allowed = g.allowed;
   o.allowed_words = (int)((g.V + 31) / 32);
-  o.lse_part = g.lse ? reinterpret_cast<uint2*>(ws + g.sync_bytes + g.heads_bytes + g.region0_bytes +
-                                                g.region1_bytes)
-                     : nullptr;
+  o.lse_part = (g.lse || g.smp.need_norm)
+                   ? reinterpret_cast<uint2*>(ws + g.sync_bytes + g.heads_bytes + g.region0_bytes +
+                                              g.region1_bytes)
+                   : nullptr;
+  o.smp = g.smp;
   return o;
 }
 }  // namespace lmtopk

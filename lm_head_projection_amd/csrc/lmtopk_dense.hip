@@ -61,6 +61,8 @@ __global__ __launch_bounds__(1024) void k_dense_chunk(DenseArgs a) {
   const int64_t row_bytes = a.H * esz;
   const int64_t base = (int64_t)blockIdx.x * C;
   const int rows_per_wave = 64 * RPL;
+  // lane m: row m's temperature (the draw's logit scale for the normaliser)
+  const float temp_v = row_temperature(a.out, lane < M ? lane : M - 1, reinterpret_cast<const float*>(a.hidden));
 
   for (int rr = 0; rr < rows_per_wave; rr += 2) {
     const int lr0 = wave * rows_per_wave + rr;
@@ -118,7 +120,8 @@ __global__ __launch_bounds__(1024) void k_dense_chunk(DenseArgs a) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r) rows[r] = ((valid >> r) & 1u) ? (int64_t)idx[r] : 0;
     const uint32_t allow = allowed_bits<RPL>(a.out, m, rows, a.hidden);
-    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm, hst, m == M - 1, allow);
+    const float zs = z_scale(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(temp_v), m)));
+    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm, hst, m == M - 1, allow, zs);
   }
   if (a.out.fused) fused_merge_tail<kFusedRM>(fused_merge_of(a.out), ssm, csm.fs, last_wg);
 }

@@ -177,6 +177,7 @@ struct alignas(16) SelectSmem {
   uint32_t wcnt[kMaxWaves];
   uint32_t cgt[kMaxWaves];
   uint32_t ceq[kMaxWaves];
+  float lse_out;  // merge_lse's result, for every thread of the workgroup
 };
 
 // Outcome of the search: keys k with (k & mask) > prefix are all selected;
@@ -683,6 +684,9 @@ struct alignas(16) FinalSmem {
   uint32_t wmin[kMaxWaves];
   uint32_t wmax[kMaxWaves];
   uint32_t hist[256];  // chunk maxima per 8-bit digit
+  // the row's result in output order, kept for the token draw
+  uint32_t out_bits[kMaxK];
+  int32_t out_idx[kMaxK];
 };
 
 // Entries [0, n) of fs are filled, [n, 4 * ceil(n / 4)) hold padding that is
@@ -721,6 +725,8 @@ __device__ __forceinline__ void rank_and_write(FinalSmem& fs, uint32_t n, uint32
     if (rank < k) {
       values[rank] = __uint_as_float(fs.bits[i]);
       indices[rank] = (int64_t)fs.idx[i];
+      fs.out_bits[rank] = fs.bits[i];
+      fs.out_idx[rank] = fs.idx[i];
     }
   }
 }
@@ -750,7 +756,8 @@ __device__ __forceinline__ void place_survivor(FinalSmem& fs, bool take, uint32_
 // ascending index order; RM slots per thread cover them (n_in <=
 // blockDim.x * RM).  `heads` (optional) holds each chunk's kHeads best
 // candidates in output order.  Writes the exact top-k sorted by (value desc,
-// index asc).
+// index asc) to values / indices, and keeps it in fs.out_bits / fs.out_idx
+// for the token draw (ordered by the caller's next barrier).
 //
 // Bounded path: a threshold T with at least k chunk maxima >= T is at most
 // the row's k-th largest value (those maxima are k distinct logits), so only
@@ -861,6 +868,8 @@ __device__ __forceinline__ void merge_final(const uint2* in, int64_t n_in, const
         if (r < k) {
           values[r] = __uint_as_float(fs.bits[i]);
           indices[r] = (int64_t)fs.idx[i];
+          fs.out_bits[r] = fs.bits[i];
+          fs.out_idx[r] = fs.idx[i];
         }
       }
       return;
@@ -897,7 +906,8 @@ __device__ __forceinline__ void merge_final(const uint2* in, int64_t n_in, const
 }
 
 // Log-sum-exp of one row (Selective Log Softmax page, section "Kernel
-// design": per-slice maxima and sums of exponentials, combined).  part[0, n)
+// design": per-slice maxima and sums of exponentials, combined), returned to
+// every thread and written to *out (unless out is null).  part[0, n)
 // holds one (max, sum) pair per wave and chunk of the row, sum = the sum of
 // exp(logit - max) over that wave's rows (max -inf: no finite rows, sum 0;
 // max +inf: an +inf logit).  With M the largest max, the row's log-sum-exp
@@ -918,7 +928,7 @@ __device__ __forceinline__ bool load_lse_pairs(const uint2* part, int n, uint2 (
   return fits;
 }
 
-__device__ __forceinline__ void merge_lse(const uint2* part, int n, float* out, SelectSmem& sm,
+__device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out, SelectSmem& sm,
                                           bool have, const uint2 (&pre)[kLsePairs]) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -955,73 +965,14 @@ __device__ __forceinline__ void merge_lse(const uint2* part, int n, float* out, 
   if (tid == 0) {
     float S = 0.f;
     for (int w = 0; w < nw; ++w) S += __uint_as_float(sm.wmin[w]);
-    *out = M == INFINITY ? INFINITY : M == -INFINITY ? -INFINITY : M + logf(S);
+    const float r = M == INFINITY ? INFINITY : M == -INFINITY ? -INFINITY : M + logf(S);
+    if (out != nullptr) *out = r;
+    sm.lse_out = r;
   }
+  lds_barrier();
+  const float r = sm.lse_out;
   lds_barrier();  // sm is reused
-}
-
-// LDS of a chunk kernel: the chunk selection's staging, and, after it, the
-// final merge of the fused path.
-union ChunkSmem {
-  HeadStage hs;
-  FinalSmem fs;
-};
-
-// What the fused final merge needs: the launch's candidate lists and heads,
-// the outputs, and a workspace counter that is zero between calls.
-struct FusedMerge {
-  uint32_t* counter;
-  const uint2* cand;   // [M][n_chunks][kc]
-  const uint2* heads;  // [M][n_chunks][kHeads]
-  float* values;       // [M][k]
-  int64_t* indices;    // [M][k]
-  int M;
-  int n_chunks;
-  int kc;
-  int k;
-  const uint2* lse_part;  // [M][n_chunks][waves] (max, sum) pairs, or null
-  float* lse;             // [M] or null
-};
-
-// Fused second pass (lm-head-topk page, section "Method": the chunk
-// candidates are merged into the final top-k).  Called by every workgroup
-// of a chunk launch (one workgroup per chunk) after it has stored its
-// candidates and heads with st_cand.  Each workgroup waits until those
-// stores are complete at device scope, then counts itself done on the
-// counter; the workgroup that counts last sees every chunk's candidates and
-// merges all M rows, then sets the counter back to zero for the next call.
-// n_chunks * kc <= blockDim.x * RM.
-// kExtras false: the launch has neither a log-sum-exp output nor a bitmask,
-// and that code is left out.
-template <int RM, bool kExtras = true>
-__device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem& sm, FinalSmem& fs,
-                                 uint32_t& last) {
-  // every store of this thread has been acknowledged (gfx9 counts stores in vmcnt)
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  lds_barrier();
-  if (threadIdx.x == 0) {
-    const uint32_t done =
-        __hip_atomic_fetch_add(f.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last = done == (uint32_t)f.n_chunks - 1u ? 1u : 0u;
-  }
-  lds_barrier();
-  if (uniform(last) == 0u) return;
-  const int64_t n_in = (int64_t)f.n_chunks * f.kc;
-  const int n_part = f.n_chunks * (int)(blockDim.x >> 6);
-  for (int m = 0; m < f.M; ++m) {
-    // the row's log-sum-exp partials are requested before the merge, which
-    // waits for its own loads meanwhile
-    uint2 pre[kLsePairs];
-    bool have = false;
-    if (kExtras && f.lse != nullptr) have = load_lse_pairs(f.lse_part + (size_t)m * n_part, n_part, pre);
-    merge_final<RM>(f.cand + (size_t)m * n_in, n_in, f.heads + (size_t)m * f.n_chunks * kHeads,
-                    f.n_chunks, f.kc, (uint32_t)f.k, f.values + (size_t)m * f.k,
-                    f.indices + (size_t)m * f.k, (int)blockDim.x, sm, fs);
-    lds_barrier();  // fs is reused by the next row
-    if (kExtras && f.lse != nullptr)
-      merge_lse(f.lse_part + (size_t)m * n_part, n_part, f.lse + m, sm, have, pre);
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(f.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return r;
 }
 
 }  // namespace lmtopk

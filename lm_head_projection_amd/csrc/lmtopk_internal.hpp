@@ -18,6 +18,27 @@ struct MergeLevel {
   int nw;        // waves per workgroup
 };
 
+// The call's token draw (lmtopk_sampling), as the kernels read it.  on == 0:
+// no draw.  need_norm: the chunk kernels form the normaliser partials of the
+// scaled logits (top-p needs lse_T).
+struct SampleParams {
+  int on;
+  int need_norm;
+  float temperature;
+  int top_k;
+  float top_p;
+  float min_p;
+  const float* temperature_rows;
+  const int32_t* top_k_rows;
+  const float* top_p_rows;
+  const float* min_p_rows;
+  uint64_t seed;
+  uint64_t offset;
+  const uint64_t* offset_device;
+  int64_t* tokens;
+  int32_t* kept;
+};
+
 // Chunking and merge plan of one call; identical for every path given
 // (M, V, k, chunk_rows).
 struct Geometry {
@@ -40,6 +61,7 @@ struct Geometry {
   size_t workspace_bytes;
   float* lse;            // this call's log-sum-exp output [M], or null (not part of the plan)
   const int32_t* allowed;  // this call's bitmask [M][ceil(V/32)], or null (not part of the plan)
+  SampleParams smp;        // this call's draw (not part of the plan)
 };
 
 // Returns 0 or an lmtopk_status code (SHAPE, K, OPTIONS).
@@ -60,12 +82,19 @@ int launch_select_chunks(const Geometry& g, const float* logits, int64_t ld, voi
                          float* values, int64_t* indices, void* stream, void* const* events);
 int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* indices,
                   void* stream);
+// Zero fill of n bytes (n % 16 == 0 handled by the caller's rounding rules:
+// any n; p 16-byte aligned).
+int launch_zero(void* p, size_t n, void* stream);
+// The binary path's 2048-row chunks (four rows per lane) serve at most this
+// many activation rows.
+constexpr int kMaxRowsWide = 2;
+
 // Largest LDS (bytes) one workgroup may use on the current device.
 int max_lds_per_block(size_t* bytes);
 
 // Upper bound of the static LDS of the chunk kernels (selection histograms
 // and the head staging); the dynamic LDS comes on top.
-constexpr size_t kChunkStaticLds = 40960;
+constexpr size_t kChunkStaticLds = 57344;
 
 // LDS bytes the scoring kernels need.
 size_t binary_lds_bytes(int64_t M, int64_t H);

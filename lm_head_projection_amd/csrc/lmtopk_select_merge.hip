@@ -103,6 +103,8 @@ __global__ __launch_bounds__(1024) void k_select_chunk(SelectArgs a) {
   const int wave = wave_id();
   const int lane = lane_id();
   const int64_t base = (int64_t)blockIdx.x * a.chunk_rows;
+  // lane m: row m's temperature (the draw's logit scale for the normaliser)
+  const float temp_v = row_temperature(a.out, lane < (int)a.M ? lane : (int)a.M - 1, a.logits);
   int32_t idx[RPL];
   uint32_t valid = 0u;
 #pragma unroll
@@ -120,7 +122,8 @@ __global__ __launch_bounds__(1024) void k_select_chunk(SelectArgs a) {
 #pragma unroll
     for (int r = 0; r < RPL; ++r) rows[r] = ((valid >> r) & 1u) ? (int64_t)idx[r] : 0;
     const uint32_t allow = allowed_bits<RPL>(a.out, m, rows, a.logits);
-    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm, hst, m == (int)a.M - 1, allow);
+    const float zs = z_scale(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(temp_v), m)));
+    chunk_select_write<RPL>(val, idx, valid, m, a.out, ssm, hst, m == (int)a.M - 1, allow, zs);
   }
   if (a.out.fused) fused_merge_tail<kFusedRM>(fused_merge_of(a.out), ssm, csm.fs, last_wg);
 }
@@ -143,6 +146,7 @@ struct MergeArgs {
   const uint2* lse_part;  // final: log-sum-exp partials [M][n_part], or null
   int n_part;
   float* lse;             // final: [M] or null
+  SampleParams smp;       // final: the token draw (smp.on == 0: none)
 };
 
 // Workgroup (segment s, row m) takes candidates [s*seg, (s+1)*seg) of row m,
@@ -160,14 +164,17 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
     __shared__ FinalSmem fs;
     uint2 pre[kLsePairs];
     bool have = false;
-    if (a.lse != nullptr) have = load_lse_pairs(a.lse_part + (size_t)m * a.n_part, a.n_part, pre);
+    if (a.lse_part != nullptr) have = load_lse_pairs(a.lse_part + (size_t)m * a.n_part, a.n_part, pre);
+    RowSample rs;
+    if (a.smp.on) rs = load_row_sample(a.smp, m);
     merge_final<RM>(in, a.n_in, a.heads ? a.heads + (size_t)m * a.n_max * kHeads : nullptr,
                     a.n_max, a.kc, (uint32_t)a.k, a.values + (size_t)m * a.k, a.indices + (size_t)m * a.k,
                     a.threads, ssm, fs);
-    if (a.lse != nullptr) {
-      lds_barrier();  // ssm is reused
-      merge_lse(a.lse_part + (size_t)m * a.n_part, a.n_part, a.lse + m, ssm, have, pre);
-    }
+    lds_barrier();  // ssm is reused; fs.out_* are complete
+    float lse = 0.f;
+    if (a.lse_part != nullptr)
+      lse = merge_lse(a.lse_part + (size_t)m * a.n_part, a.n_part, a.lse ? a.lse + m : nullptr, ssm, have, pre);
+    if (a.smp.on) sample_row(fs.out_bits, fs.out_idx, a.k, lse, rs, m, a.smp);
     return;
   }
   const int wave = wave_id();
@@ -196,6 +203,16 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
   for (int i = (int)n + (int)threadIdx.x; i < a.k; i += blockDim.x)
     out[i] = make_uint2(0u, 0xFFFFFFFFu);
 }
+// Zero fill of a workspace (a kernel, not a memset, so that graph capture
+// records a kernel node).  n16 whole 16-byte vectors, then tail bytes.
+__global__ __launch_bounds__(256) void k_zero(uint4* __restrict__ p, int64_t n16, uint8_t* tail,
+                                              int n_tail) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (blockIdx.x == 0 && (int)threadIdx.x < n_tail) tail[threadIdx.x] = 0;
+}
+
 namespace {
 
 void (*select_kernel(int rpl))(SelectArgs) {
@@ -244,6 +261,20 @@ int launch_pack(const void* w, int w_is_bf16, int64_t V, int64_t H, void* wq, fl
                                : reinterpret_cast<const void*>(k_pack<false>);
   return (int)hipLaunchKernel(kern, grid, block, args, 0, static_cast<hipStream_t>(stream));
 }
+int launch_zero(void* p, size_t n, void* stream) {
+  const int64_t n16 = (int64_t)(n / 16);
+  uint8_t* tail = static_cast<uint8_t*>(p) + n16 * 16;
+  const int n_tail = (int)(n % 16);
+  int64_t blocks = (n16 + 255) / 256;
+  blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
+  uint4* a_p = static_cast<uint4*>(p);
+  int64_t a_n16 = n16;
+  uint8_t* a_tail = tail;
+  int a_nt = n_tail;
+  void* args[] = {&a_p, &a_n16, &a_tail, &a_nt};
+  return (int)hipLaunchKernel(reinterpret_cast<const void*>(k_zero), dim3((unsigned)blocks), dim3(256),
+                              args, 0, static_cast<hipStream_t>(stream));
+}
 int launch_select_chunks(const Geometry& g, const float* logits, int64_t ld, void* workspace,
                          float* values, int64_t* indices, void* stream, void* const* events) {
   SelectArgs a;
@@ -281,7 +312,10 @@ int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* in
     a.indices = indices;
     a.lse = g.lse;
     a.n_part = g.n_chunks * g.nw;
-    a.lse_part = reinterpret_cast<const uint2*>(ws + g.region0_bytes + g.region1_bytes);
+    a.lse_part = (g.lse || g.smp.need_norm)
+                     ? reinterpret_cast<const uint2*>(ws + g.region0_bytes + g.region1_bytes)
+                     : nullptr;
+    a.smp = g.smp;
     auto kern = merge_kernel(L.rm);
     if (!kern) return (int)hipErrorInvalidValue;
     const hipError_t e = launch1(kern, dim3(L.n_seg, (unsigned)g.M), dim3(64 * L.nw), 0, stream, a);

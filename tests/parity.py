@@ -20,6 +20,7 @@ terms of total magnitude mag: n * 2^-24 * mag, with n and mag given by the
 caller for its accumulation order.
 """
 
+import math
 import os
 
 import numpy as np
@@ -120,3 +121,60 @@ def dense_eps_fn(hidden_f32, weight_rows_fn, bias, H):
             mag = mag + np.abs(np.asarray(bias, dtype=np.float64)[ix])
         return (H / 64 + 8) * U * mag
     return fn
+
+
+def check_draw(r, gpu_token, gpu_kept, top_k, top_p, min_p, k, eps_z=0.0, tol_p=2e-4, tol_m=1e-4):
+    """Check one row's GPU draw against the oracle's row result r
+    (oracle.sample_row).
+
+    The keep-set size must be one the oracle's decisions allow: a decision
+    within the fp32 allowance of its threshold (top-p mass within tol_p,
+    min-p ratio within tol_m relative, or the scaled logits' own error eps_z
+    on the ratio) may go either way, every other one must match.  The token
+    must be a kept survivor whose oracle score z + g is within the fp32 bound
+    of the best kept score, so where the oracle's winner leads by more than
+    that bound the token equals the oracle's.  Returns True when the GPU
+    differs from the oracle only inside those allowances."""
+    idx = [int(x) for x in r["indices"]]
+    if r["z"] is None:  # greedy
+        assert int(gpu_token) == r["token"] and int(gpu_kept) == 1, (gpu_token, r["token"], gpu_kept)
+        return False
+    z, lse = r["z"], r["lse"]
+    limit = k if (top_k <= 0 or top_k >= k) else int(top_k)
+    below = np.concatenate([[0.0], np.cumsum(np.exp(z - lse))])  # mass before position i
+    ok = set()
+    can_keep = True
+    for n in range(1, limit + 1):
+        if not can_keep:
+            break
+        if n == limit:
+            ok.add(n)
+            break
+        zi = z[n]
+        if zi == -np.inf:
+            ok.add(n)
+            break
+        stop_must = stop_may = False
+        if top_p < 1.0:
+            d = below[n] - top_p
+            stop_must |= d > tol_p
+            stop_may |= d > -tol_p
+        if min_p > 0.0:
+            ratio = math.exp(zi - z[0])
+            tol = tol_m * max(ratio, min_p) + 2 * eps_z * ratio
+            stop_must |= ratio < min_p - tol
+            stop_may |= ratio < min_p + tol
+        if stop_may:
+            ok.add(n)
+        can_keep = not stop_must
+    assert int(gpu_kept) in ok, f"keep-set size {int(gpu_kept)} not in {sorted(ok)} (oracle {r['kept']})"
+    n = int(gpu_kept)
+    assert int(gpu_token) in idx[:n], f"token {int(gpu_token)} outside the kept prefix"
+    pos = idx.index(int(gpu_token))
+    score = np.array([z[i] + oracle.gumbel(oracle.draw_uniform(r["seed"], r["row"], r["offset"], idx[i]))
+                      for i in range(n)])
+    bound = 4.0 * (U * 4 * (np.abs(z[:n]) + np.abs(score - z[:n])) + 2.0 ** -21) + 2 * eps_z
+    best = int(np.argmax(score))
+    assert score[pos] >= score[best] - (bound[pos] + bound[best]), \
+        f"token {int(gpu_token)} (score {score[pos]!r}) vs best {idx[best]} ({score[best]!r})"
+    return int(gpu_token) != r["token"] or n != r["kept"]

@@ -6,7 +6,9 @@ integers that the library must never dereference."""
 import ctypes
 import os
 import re
+import shutil
 import subprocess
+import tempfile
 
 import pytest
 
@@ -87,14 +89,65 @@ def _select(**kw):
                                  a["indices"], a["ws"], a["ws_bytes"], a["opt"], a["stream"])
 
 
-def opt(chunk_rows=0, reserved=0, lse=None, allowed=None):
-    return ctypes.byref(lt._Options(chunk_rows, reserved, None, lse, allowed))
+_KEEP = []
 
 
-def test_options_layout_matches_the_header():
-    # chunk_rows, reserved (int32 each), then three pointers: score_events, lse, allowed
-    assert ctypes.sizeof(lt._Options) == 8 + 3 * ctypes.sizeof(ctypes.c_void_p)
-    assert lt._Options.lse.offset == 16 and lt._Options.allowed.offset == 24
+def opt(chunk_rows=0, reserved=0, lse=None, allowed=None, sampling=None):
+    sp = ctypes.pointer(sampling) if sampling is not None else None
+    o = lt._Options(chunk_rows, reserved, None, lse, allowed, sp)
+    _KEEP.append((o, sampling))
+    return ctypes.byref(o)
+
+
+def smp(**kw):
+    c = lt._SamplingC()
+    c.temperature, c.top_k, c.top_p, c.min_p = 1.0, 0, 1.0, 0.0
+    c.tokens = A
+    for key, v in kw.items():
+        setattr(c, key, v)
+    return c
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs a C compiler")
+def test_struct_layouts_match_the_header():
+    """offsetof of every field, compiled from include/lmtopk.h, equals the
+    binding's ctypes layout."""
+    fields = {"lmtopk_options": lt._Options, "lmtopk_sampling": lt._SamplingC}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "lmtopk.h"', "int main(void) {"]
+    for cname, py in fields.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines.append("return 0; }")
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "l.c"), os.path.join(d, "l")
+        open(src, "w").write("\n".join(lines))
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), src, "-o", exe],
+                       check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l}
+    for cname, py in fields.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py)
+        for f, _ in py._fields_:
+            assert got[(cname, f)] == getattr(py, f).offset, (cname, f)
+
+
+@pytest.mark.parametrize("entry", ["binary", "dense", "select"])
+def test_sampling_arguments_are_checked_before_any_launch(entry):
+    call = {"binary": _binary, "dense": _dense, "select": _select}[entry]
+    assert call(opt=opt(sampling=smp(tokens=None))) == NULL
+    assert call(opt=opt(sampling=smp(tokens=ODD))) == ALIGN
+    assert call(opt=opt(sampling=smp(kept=ODD))) == ALIGN
+    assert call(opt=opt(sampling=smp(temperature_rows=ODD))) == ALIGN
+    assert call(opt=opt(sampling=smp(offset_device=ODD))) == ALIGN
+    assert call(opt=opt(sampling=smp(top_k=11))) == OPTIONS      # above the call's k = 10
+
+
+def test_workspace_init_rejects():
+    lib = lt._lib
+    assert lib.lmtopk_workspace_init(None, 256, None) == NULL
+    assert lib.lmtopk_workspace_init(ODD, 256, None) == ALIGN
+    assert lib.lmtopk_workspace_init(A, 0, None) == OK   # nothing to fill, nothing launched
 
 
 @pytest.mark.parametrize("entry", ["binary", "dense", "select"])
@@ -113,6 +166,7 @@ def test_misaligned_lse_or_bitmask_is_rejected_before_any_launch(entry):
     (dict(act_q=ODD), ALIGN), (dict(wq=ODD), ALIGN), (dict(bias=ODD), ALIGN), (dict(values=ODD), ALIGN),
     (dict(ws=None), WORKSPACE), (dict(ws_bytes=16), WORKSPACE),
     (dict(opt=opt(100)), OPTIONS), (dict(opt=opt(4096)), OPTIONS), (dict(opt=opt(8192)), OPTIONS), (dict(opt=opt(0, 1)), OPTIONS),
+    (dict(M=3, opt=opt(2048)), OPTIONS), (dict(M=8, V=5000, opt=opt(2048)), OPTIONS),
 ])
 def test_binary_rejects(kw, code):
     assert _binary(**kw) == code

@@ -278,3 +278,51 @@ def test_cfg5_sweep_with_bias(flagship, M, k):
     v, i, _ = c.check(k, rows=rows)
     if k == 1:
         assert np.array_equal(i.cpu().numpy()[:, 0], np.argmax(c.L[:M], axis=1))
+
+
+# ---------------------------------------------------------------------------
+# chunk sizes x optional outputs: every binary kernel instance that exists
+# runs (2048-row chunks, four rows per lane, serve M <= 2; from three rows on
+# the library refuses them)
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def wide_case():
+    return Case(8, 1024, 20001, seed=9, with_bias=True)
+
+
+def _mask(M, V, seed):
+    rng = np.random.default_rng(seed)
+    allowed = rng.random((M, V)) < 0.5
+    pad = np.zeros((M, ((V + 31) // 32) * 32), dtype=bool)
+    pad[:, :V] = allowed
+    return np.packbits(pad, axis=1, bitorder="little").view("<i4")
+
+
+@pytest.mark.parametrize("extras", ["none", "lse_and_mask"])
+@pytest.mark.parametrize("chunk_rows", [0, 2048])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
+def test_chunk_sizes_and_extras(wide_case, M, chunk_rows, extras):
+    c, k = wide_case, 50
+    rows = list(range(M))
+    aq, sc = c.d_act[:M].contiguous(), c.d_scale[:M].contiguous()
+    lse = torch.empty(M, device="cuda") if extras != "none" else None
+    bm = _mask(M, c.V, M) if extras != "none" else None
+    kw = dict(bias=c.d_bias, k=k, vocab_size=c.V, chunk_rows=chunk_rows, lse=lse,
+              allowed=torch.from_numpy(bm).cuda() if bm is not None else None)
+    if chunk_rows == 2048 and M > 2:
+        with pytest.raises(lt.LmTopkError) as e:
+            lt.lm_head_topk_binary(aq, sc, c.wq, c.ws, **kw)
+        assert e.value.status == 8  # LMTOPK_ERR_OPTIONS
+        return
+    v, i = lt.lm_head_topk_binary(aq, sc, c.wq, c.ws, **kw)
+    torch.cuda.synchronize()
+    L = c.L[:M] if bm is None else oracle.apply_allowed(c.L[:M], bm)
+    eps = binary_eps_fn(c.act_q[:M], c.act_scale[:M], lambda ix: c.scales[ix], c.bias, c.G)
+    compare_end_to_end(L, v.cpu().numpy(), i.cpu().numpy(), k, RTOL_BINARY, eps)
+    if lse is not None:
+        want = oracle.logsumexp_rows(L)
+        tol = 1e-5 + 2.0**-22 * np.abs(want) + np.array([eps(m, np.arange(c.V)).max() for m in range(M)])
+        assert np.all(np.abs(lse.cpu().numpy() - want) <= tol)
+    # the chunk size does not change a bit
+    v0, i0 = lt.lm_head_topk_binary(aq, sc, c.wq, c.ws, **{**kw, "chunk_rows": 256})
+    assert torch.equal(i0, i) and torch.equal(v0.view(torch.int32), v.view(torch.int32))

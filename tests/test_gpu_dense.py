@@ -97,3 +97,11 @@ def test_dense_repeat_and_chunk_invariance():
     for m in range(4):
         v1, i1 = lt.lm_head_topk_dense(h_dev[m:m + 1].contiguous(), w_dev, k=50, bias=b_dev)
         assert torch.equal(i1[0], i0[m]) and torch.equal(v1[0].view(torch.int32), v0[m].view(torch.int32))
+
+
+@pytest.mark.slow
+def test_dense_bf16_flagship_shape():
+    """Dense bf16 head at the measured shape: M=1, H=5,120, V=248,320, k=50
+    (lm-head-topk page, section "Measured": the bf16 comparison path)."""
+    relaxed = check(1, 5120, 248320, 50, 0, "bf16", False)
+    assert relaxed <= 2
