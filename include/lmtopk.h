@@ -304,6 +304,28 @@ lmtopk_status lmtopk_select(const float* logits, int64_t M, int64_t V,
                             size_t workspace_bytes, const lmtopk_options* opt,
                             void* stream);
 
+/*
+ * lmtopk_binary without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, checks, kernels and
+ * results as lmtopk_binary; its workspace is a device array inside the
+ * library, LMTOPK_NOALLOC_SCRATCH_BYTES bytes per GPU, held from its first
+ * use on a GPU until the process ends.  The call itself allocates nothing.
+ * Calls on one GPU share that array: calls that overlap in time on one GPU
+ * (several streams or threads at once) race and give wrong results; order
+ * them.  The first call on a GPU also enqueues one small fill kernel on
+ * `stream` that clears the array's completion counter.
+ * Errors: as lmtopk_binary; WORKSPACE when lmtopk_workspace_bytes for these
+ * sizes and options exceeds LMTOPK_NOALLOC_SCRATCH_BYTES.
+ */
+#define LMTOPK_NOALLOC_SCRATCH_BYTES (8u << 20)
+lmtopk_status lmtopk_binary_noalloc(const int8_t* act_q, const float* act_scale,
+                                    const void* wq, const float* wscale,
+                                    const float* bias, int64_t M, int64_t V,
+                                    int64_t H, int32_t group_size, int32_t k,
+                                    float* values, int64_t* indices,
+                                    const lmtopk_options* opt, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-HIP_SOURCES = ["lmtopk_binary.hip", "lmtopk_dense.hip", "lmtopk_select_merge.hip"]
+HIP_SOURCES = ["lmtopk_binary.hip", "lmtopk_dense.hip", "lmtopk_select_merge.hip",
+               "lmtopk_noalloc.hip"]
 # Packed-fp32 instructions stay off in every device compile.
 DEVICE_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",

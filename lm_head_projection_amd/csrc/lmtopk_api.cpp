@@ -237,30 +237,69 @@ static void* const* score_events(const lmtopk_options* opt) {
   return opt ? static_cast<void* const*>(opt->score_events) : nullptr;
 }
 
-lmtopk_status lmtopk_binary(const int8_t* act_q, const float* act_scale, const void* wq,
-                            const float* wscale, const float* bias, int64_t M, int64_t V,
-                            int64_t H, int32_t group_size, int32_t k, float* values,
-                            int64_t* indices, void* workspace, size_t workspace_bytes,
-                            const lmtopk_options* opt, void* stream) {
+// The binary call in two phases: every argument check (the workspace only
+// as a size and an alignment), then the launches.  lmtopk_binary and
+// lmtopk_binary_noalloc share both.
+static lmtopk_status binary_checks(const int8_t* act_q, const float* act_scale, const void* wq,
+                                   const float* wscale, const float* bias, int64_t M, int64_t V,
+                                   int64_t H, int32_t group_size, int32_t k, float* values,
+                                   int64_t* indices, const void* workspace,
+                                   size_t workspace_bytes, const lmtopk_options* opt, Geometry* g) {
   if (!act_q || !act_scale || !wq || !wscale) return LMTOPK_ERR_NULL;
-  Geometry g;
-  lmtopk_status st =
-      common_checks(workspace, workspace_bytes, values, indices, opt, M, V, k, &g);
+  lmtopk_status st = common_checks(workspace, workspace_bytes, values, indices, opt, M, V, k, g);
   if (st) return st;
   if (H < 1) return LMTOPK_ERR_SHAPE;
   if (group_size != LMTOPK_GROUP_SIZE || H % LMTOPK_GROUP_SIZE != 0) return LMTOPK_ERR_GROUP;
   if (M * H > LMTOPK_MAX_BINARY_MH) return LMTOPK_ERR_SHAPE;
-  if (g.rpl > 1 && M > lmtopk::kMaxRowsWide) return LMTOPK_ERR_OPTIONS;
+  if (g->rpl > 1 && M > lmtopk::kMaxRowsWide) return LMTOPK_ERR_OPTIONS;
   if (!lmtopk::aligned16(act_q) || !lmtopk::aligned16(act_scale) || !lmtopk::aligned16(wq) ||
       !lmtopk::aligned16(wscale) || (bias && !lmtopk::aligned16(bias)))
     return LMTOPK_ERR_ALIGN;
   size_t lds_max = 0;
   if (lmtopk::max_lds_per_block(&lds_max)) return LMTOPK_ERR_HIP;
   if (lmtopk::binary_lds_bytes(M, H) + lmtopk::kChunkStaticLds > lds_max) return LMTOPK_ERR_SHAPE;
+  return LMTOPK_OK;
+}
+
+static lmtopk_status binary_launch(const Geometry& g, const int8_t* act_q, const float* act_scale,
+                                   const void* wq, const float* wscale, const float* bias, int64_t H,
+                                   float* values, int64_t* indices, void* workspace,
+                                   const lmtopk_options* opt, void* stream) {
   const int e =
       lmtopk::launch_binary_chunks(g, act_q, act_scale, wq, wscale, bias, H, workspace, values,
                                    indices, stream, score_events(opt));
   return finish(g, e, workspace, values, indices, stream);
+}
+
+lmtopk_status lmtopk_binary(const int8_t* act_q, const float* act_scale, const void* wq,
+                            const float* wscale, const float* bias, int64_t M, int64_t V,
+                            int64_t H, int32_t group_size, int32_t k, float* values,
+                            int64_t* indices, void* workspace, size_t workspace_bytes,
+                            const lmtopk_options* opt, void* stream) {
+  Geometry g;
+  const lmtopk_status st = binary_checks(act_q, act_scale, wq, wscale, bias, M, V, H, group_size,
+                                         k, values, indices, workspace, workspace_bytes, opt, &g);
+  if (st) return st;
+  return binary_launch(g, act_q, act_scale, wq, wscale, bias, H, values, indices, workspace, opt,
+                       stream);
+}
+
+lmtopk_status lmtopk_binary_noalloc(const int8_t* act_q, const float* act_scale, const void* wq,
+                                    const float* wscale, const float* bias, int64_t M, int64_t V,
+                                    int64_t H, int32_t group_size, int32_t k, float* values,
+                                    int64_t* indices, const lmtopk_options* opt, void* stream) {
+  Geometry g;
+  // the scratch array stands in for the workspace: checked as one of
+  // LMTOPK_NOALLOC_SCRATCH_BYTES bytes at a 256-byte aligned address
+  const lmtopk_status st =
+      binary_checks(act_q, act_scale, wq, wscale, bias, M, V, H, group_size, k, values, indices,
+                    reinterpret_cast<const void*>(static_cast<uintptr_t>(256)),
+                    (size_t)LMTOPK_NOALLOC_SCRATCH_BYTES, opt, &g);
+  if (st) return st;
+  void* scratch = nullptr;
+  if (lmtopk::noalloc_scratch(&scratch, stream)) return LMTOPK_ERR_HIP;
+  return binary_launch(g, act_q, act_scale, wq, wscale, bias, H, values, indices, scratch, opt,
+                       stream);
 }
 
 lmtopk_status lmtopk_dense(const void* hidden, const void* weight, lmtopk_dtype dtype,

@@ -89,6 +89,12 @@ int launch_zero(void* p, size_t n, void* stream);
 // many activation rows.
 constexpr int kMaxRowsWide = 2;
 
+// The device address of the current device's scratch array (the workspace of
+// lmtopk_binary_noalloc, LMTOPK_NOALLOC_SCRATCH_BYTES bytes), found on its
+// first use on that device, when its completion counter is also cleared by a
+// kernel on `stream`.  Returns a hipError_t value.
+int noalloc_scratch(void** ptr, void* stream);
+
 // Largest LDS (bytes) one workgroup may use on the current device.
 int max_lds_per_block(size_t* bytes);
 
