@@ -11,6 +11,14 @@ merge in the launch's last workgroup).  The packed head is
 198.7 MB, smaller than the 256 MB Infinity Cache, so the timed loop rotates
 --copies bitwise-identical packed copies (4 x 198.7 MB) to make the weights
 come from HBM; a single-copy (cache-served) figure is reported beside it.
+--sample adds the token draw of the logits-processor page's usage example
+(temperature 0.7, top_k 50, top_p 0.9) to every call.
+
+Order: inputs; the auxiliary measurements (graph replay, cache-served single
+copy, the box's plain read and copy rates), which also bring an idle GPU to
+its steady clocks; the --warmup untimed steps; the --steps timed steps; the
+scoring kernel's own duration (events on its dispatch); the materialized
+comparison; the CPU oracle.
 
 Printed: one JSON line (see the end of main()).  Kernel times come from HIP
 events recorded on the stream the kernels run on; `roofline.traffic` comes from
@@ -44,7 +52,8 @@ SCORE_KERNEL = "k_binary_chunk"
 COPY_BYTES = 1 << 30
 KERNEL_SOURCES = ["lm_head_projection_amd/csrc/lmtopk_binary.hip",
                   "lm_head_projection_amd/csrc/lmtopk_chunk.hpp",
-                  "lm_head_projection_amd/csrc/lmtopk_device.hpp"]
+                  "lm_head_projection_amd/csrc/lmtopk_device.hpp",
+                  "lm_head_projection_amd/csrc/lmtopk_sample.hpp"]
 
 
 def kernel_source_hash():
@@ -70,6 +79,8 @@ def parse_args():
     p.add_argument("--bias", action="store_true")
     p.add_argument("--chunk-rows", type=int, default=0)
     p.add_argument("--lse", action="store_true", help="also return each row's log-sum-exp")
+    p.add_argument("--sample", action="store_true",
+                   help="also draw one token per row (temperature 0.7, top_k 50, top_p 0.9)")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-reps", type=int, default=5, help="oracle calls timed for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -227,6 +238,17 @@ def algorithmic_score_bytes(M, V, H, k, bias, chunk_rows, lt):
     return wq_b + ws_b + (4 * V if bias else 0) + M * H + 4 * M + M * n_chunks * kc * 8
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(args, W, act_q, act_scale, bias):
     import numpy as np
     import oracle
@@ -247,10 +269,11 @@ def cpu_baseline(args, W, act_q, act_scale, bias):
     threads = max([i.get("num_threads", 1) for i in blas] or [1])
     per_call = statistics.median(times)
     return {"value": per_call * 1e6 / M, "unit": "µs/token", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{args.cpu_reps} full oracle calls (fp64 dequantized projection of all "
                       f"{V} rows + stable top-{args.k}) at M={M}; median {per_call:.2f} s per call; "
                       f"BLAS threads {threads}, NumPy elementwise single-threaded; host has "
-                      f"{len(os.sched_getaffinity(0))} cores"}
+                      f"{len(os.sched_getaffinity(0))} cores ({cpu_model()})"}
 
 
 def time_calls(hip, stream, call, n, per_step_events):
@@ -333,12 +356,26 @@ def main():
 
     hip = Hip()
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    tokens = torch.empty(M, dtype=torch.int64, device=dev) if args.sample else None
 
     def call(i, ev, rot=args.copies):
         wq, ws = copies[i % rot]
+        smp = lt.Sampling(0.7, min(50, k), 0.9, 0.0, seed=args.seed, offset=i) if args.sample else None
         lt.lm_head_topk_binary(d_aq, d_as, wq, ws, bias=d_b, k=k, vocab_size=V,
                                chunk_rows=args.chunk_rows, out=(vals, idx), workspace=work,
-                               score_events=ev, lse=lse)
+                               score_events=ev, lse=lse, sampling=smp, tokens=tokens)
+
+    # auxiliary measurements first (they also bring an idle GPU to its steady
+    # clocks before the timed steps)
+    aux_calls = max(args.steps, 1000)
+    graph_us = graph_replay_us(args, call, hip, stream, vals, idx)
+    # one packed copy only: served from the 256 MB Infinity Cache
+    warm_ms, _, _ = time_calls(hip, stream, lambda i, ev: call(i, ev, 1), aux_calls, False)
+    warm_us = warm_ms / aux_calls * 1e3
+    read_gbps = plain_read_gbps(hip, stream, dev)
+    stream_gbps = plain_copy_gbps(hip, stream, dev)
+    log(f"hipGraph replay {graph_us} us/step; single-copy (cache) {warm_us:.2f} us/step; "
+        f"plain 1 GiB read {read_gbps:.0f} GB/s, copy {stream_gbps:.0f} GB/s (read + written)")
 
     for i in range(args.warmup):
         call(i, None)
@@ -353,22 +390,16 @@ def main():
     ms_per_step = total_ms / args.steps
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (GPU events); wall {wall * 1e3:.1f} ms")
 
-    # kernel split with per-step events (same rotation)
-    _, score_ms, merge_ms = time_calls(hip, stream, call, args.steps, per_step_events=True)
+    # the scoring kernel's own duration: events attached to its dispatch, on
+    # the stream it runs on (same rotation, right after the timed steps)
+    _, score_ms, merge_ms = time_calls(hip, stream, call, aux_calls, per_step_events=True)
     score_us = statistics.mean(score_ms) * 1e3
     merge_us = statistics.mean(merge_ms) * 1e3
-    # one packed copy only: served from the 256 MB Infinity Cache
-    warm_ms, _, _ = time_calls(hip, stream, lambda i, ev: call(i, ev, 1), args.steps, False)
-    warm_us = warm_ms / args.steps * 1e3
-    log(f"scoring kernel {score_us:.2f} us, then {merge_us:.2f} us to the call's closing event; "
-        f"single-copy (cache) {warm_us:.2f} us/step")
+    log(f"scoring kernel {score_us:.2f} us, then {merge_us:.2f} us to the call's closing event")
     # per-call spread: scoring kernel start to the call's closing event
     call_us = sorted((a + b) * 1e3 for a, b in zip(score_ms, merge_ms))
     pct = lambda q: round(call_us[min(len(call_us) - 1, int(q * len(call_us)))], 3)
-    graph_us = graph_replay_us(args, call, hip, stream, vals, idx)
-    log(f"per call p10/p50/p90 {pct(0.1)}/{pct(0.5)}/{pct(0.9)} us; hipGraph replay {graph_us} us/step")
-    stream_gbps = plain_copy_gbps(hip, stream, dev)
-    log(f"plain 1 GiB copy: {stream_gbps:.0f} GB/s read + written")
+    log(f"per call p10/p50/p90 {pct(0.1)}/{pct(0.5)}/{pct(0.9)} us")
 
     # (plain_copy_gbps above also serves as the counter calibration of
     # --summarize-pmc: a copy of known size)
@@ -392,9 +423,11 @@ def main():
         "dtype": "int8 x 1-bit integer dots, fp32 accumulate",
         "data": "synthetic (seeded N(0,1)/sqrt(H) head and hidden rows; int8 symmetric activations)",
         "config": {"workload": f"binary head V={V} H={H} k={k} M={M} group 128"
-                               f"{' +bias' if args.bias else ''}{' +lse' if args.lse else ''}, "
+                               f"{' +bias' if args.bias else ''}{' +lse' if args.lse else ''}"
+                               f"{' +sample(T 0.7, top_k 50, top_p 0.9)' if args.sample else ''}, "
                                f"{args.copies} rotated packed copies",
                    "V": V, "H": H, "k": k, "M": M, "bias": bool(args.bias), "lse": bool(args.lse),
+                   "sample": bool(args.sample),
                    "chunk_rows": args.chunk_rows or 1024, "rotated_copies": args.copies},
         "gbps": round(head_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "head_bytes": head_bytes,
@@ -406,6 +439,7 @@ def main():
                        "kernel_end_to_call_event": round(merge_us, 3)},
         "per_call_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
         "graph_replay_us_per_step": graph_us,
+        "plain_read_gbps_1gib": round(read_gbps, 1),
         "plain_copy_gbps_1gib": round(stream_gbps, 1),
         "cache_served_single_copy": {"us_per_token": round(warm_us / M, 3),
                                      "gbps": round(head_bytes / (warm_us * 1e-6) / 1e9, 1)},
@@ -446,6 +480,26 @@ def graph_replay_us(args, call, hip, stream, vals, idx):
                          False)
     del g
     return round(t / (reps * args.copies) * 1e3, 3)
+
+
+def plain_read_gbps(hip, stream, dev):
+    """Achievable HBM read rate on this machine: a plain non-temporal streaming
+    read of 1 GiB (lm_head_projection_amd/csrc/probe_read.hip), 256
+    workgroups of 1,024 threads, best of 3 runs of 10 launches."""
+    import torch
+    path = os.path.join(ROOT, "lm_head_projection_amd", "_lib", "libprobe_read.so")
+    lib = ctypes.CDLL(path)
+    lib.probe_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                               ctypes.c_void_p]
+    buf = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(256 * 4, dtype=torch.int32, device=dev)
+    run = lambda i, ev: lib.probe_read(buf.data_ptr(), COPY_BYTES, sink.data_ptr(), 256, stream)
+    for i in range(3):
+        if run(i, None) != 0:
+            raise RuntimeError("probe_read launch failed")
+    best = min(time_calls(hip, stream, run, 10, False)[0] for _ in range(3))
+    del buf, sink
+    return COPY_BYTES / (best / 10 * 1e-3) / 1e9
 
 
 def plain_copy_gbps(hip, stream, dev):

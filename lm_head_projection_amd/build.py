@@ -5,6 +5,8 @@
 The HIP translation units (kernels + launchers, one per path) are compiled
 by hipcc for gfx950 in parallel; the C ABI layer is plain host C++ compiled
 by g++; hipcc links them all into lm_head_projection_amd/_lib/liblmtopk.so.
+The benchmark's read-rate probe (csrc/probe_read.hip) is built beside it as
+_lib/libprobe_read.so.
 """
 
 import os
@@ -19,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(OUT_DIR, "liblmtopk.so")
+PROBE_LIB = os.path.join(OUT_DIR, "libprobe_read.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
@@ -64,6 +67,10 @@ def build(verbose=False):
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    # the benchmark's read-rate probe: a library of its own, not liblmtopk
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, *DEVICE_FLAGS, "-shared", os.path.join(CSRC, "probe_read.hip"), "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

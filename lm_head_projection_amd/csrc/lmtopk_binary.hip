@@ -107,7 +107,9 @@ static_assert(sizeof(SelectSmem) + sizeof(ChunkSmem) + 16 <= kChunkStaticLds,
 // Quads of weight loads in flight per wave.
 constexpr int kQuadBuffers = 2;
 
-template <int M, int R, bool kExtras>
+// kExtras: a log-sum-exp output or a bitmask; kSample (implies kExtras): a
+// token draw.  Calls without them run instances with that code left out.
+template <int M, int R, bool kExtras, bool kSample = false>
 __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs a) {
   extern __shared__ __align__(16) uint8_t dyn_lds[];
   __shared__ SelectSmem ssm;
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   // memory round trip)
   const float act_sv = a.act_scale[lane < M ? lane : M - 1];
   // lane m: row m's temperature (the draw's logit scale for the normaliser)
-  const float temp_v = kExtras ? row_temperature(a.out, lane < M ? lane : M - 1, a.act_scale) : 1.f;
+  const float temp_v = kSample ? row_temperature(a.out, lane < M ? lane : M - 1, a.act_scale) : 1.f;
   // the call's bitmask bits of this lane's rows, per activation row
   uint32_t allow[M];
   {
@@ -374,37 +376,48 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     float val[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) val[r] = fmaf(acc[r][m], s, bias_v[r]);
-    const float zs = z_scale(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(temp_v), m)));
+    const float zs =
+        kSample ? z_scale(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(temp_v), m))) : 1.f;
     chunk_select_write<R, kExtras>(val, idx, valid, m, a.out, ssm, hst, m == M - 1, allow[m], zs);
   }
-  if (a.out.fused) fused_merge_tail<kFusedRM, kExtras>(fused_merge_of(a.out), ssm, csm.fs, last_wg);
+  if (a.out.fused)
+    fused_merge_tail<kFusedRM, kExtras, kSample>(fused_merge_of(a.out), ssm, csm.fs, last_wg);
 }
 namespace {
 
-// kExtras: a log-sum-exp output, a bitmask or a token draw (kernels without
-// them leave that code out)
+// mode 0: plain; 1: log-sum-exp output or bitmask; 2: also a token draw
+// (kernels without them leave that code out)
+template <int M, int R>
+void (*binary_kernel_mr(int mode))(BinaryArgs) {
+  switch (mode) {
+    case 0: return k_binary_chunk<M, R, false>;
+    case 1: return k_binary_chunk<M, R, true>;
+    case 2: return k_binary_chunk<M, R, true, true>;
+  }
+  return nullptr;
+}
 // 2048-row chunks (4 rows per lane) exist for one and two rows only: from
 // three rows on their accumulators and weight buffers no longer fit the
 // registers (the host refuses that option there).
 template <int M>
-void (*binary_kernel_m(int rpl, bool extras))(BinaryArgs) {
-  if (rpl == 1) return extras ? k_binary_chunk<M, 1, true> : k_binary_chunk<M, 1, false>;
+void (*binary_kernel_m(int rpl, int mode))(BinaryArgs) {
+  if (rpl == 1) return binary_kernel_mr<M, 1>(mode);
   if constexpr (M <= kMaxRowsWide) {
-    if (rpl == 4) return extras ? k_binary_chunk<M, 4, true> : k_binary_chunk<M, 4, false>;
+    if (rpl == 4) return binary_kernel_mr<M, 4>(mode);
   }
   return nullptr;
 }
 
-void (*binary_kernel(int M, int rpl, bool extras))(BinaryArgs) {
+void (*binary_kernel(int M, int rpl, int mode))(BinaryArgs) {
   switch (M) {
-    case 1: return binary_kernel_m<1>(rpl, extras);
-    case 2: return binary_kernel_m<2>(rpl, extras);
-    case 3: return binary_kernel_m<3>(rpl, extras);
-    case 4: return binary_kernel_m<4>(rpl, extras);
-    case 5: return binary_kernel_m<5>(rpl, extras);
-    case 6: return binary_kernel_m<6>(rpl, extras);
-    case 7: return binary_kernel_m<7>(rpl, extras);
-    case 8: return binary_kernel_m<8>(rpl, extras);
+    case 1: return binary_kernel_m<1>(rpl, mode);
+    case 2: return binary_kernel_m<2>(rpl, mode);
+    case 3: return binary_kernel_m<3>(rpl, mode);
+    case 4: return binary_kernel_m<4>(rpl, mode);
+    case 5: return binary_kernel_m<5>(rpl, mode);
+    case 6: return binary_kernel_m<6>(rpl, mode);
+    case 7: return binary_kernel_m<7>(rpl, mode);
+    case 8: return binary_kernel_m<8>(rpl, mode);
   }
   return nullptr;
 }
@@ -431,7 +444,8 @@ int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* ac
   a.Q = (a.G + 3) / 4;
   a.tiles_per_chunk = g.chunk_rows / 64;
   a.out = chunk_out(g, workspace, values, indices);
-  auto kern = binary_kernel((int)g.M, g.rpl, g.lse != nullptr || g.allowed != nullptr || g.smp.on);
+  const int mode = g.smp.on ? 2 : (g.lse != nullptr || g.allowed != nullptr) ? 1 : 0;
+  auto kern = binary_kernel((int)g.M, g.rpl, mode);
   if (!kern) return (int)hipErrorInvalidValue;
   return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), binary_lds_bytes(g.M, H), stream, a,
                       events);

@@ -47,9 +47,9 @@ struct FusedMerge {
 // merges all M rows, then sets the counter back to zero for the next call.
 // n_chunks * kc <= blockDim.x * RM.  With a token draw, each row's token is
 // drawn right after its merge (sample_row).
-// kExtras false: the launch has no log-sum-exp output, bitmask or draw, and
-// that code is left out.
-template <int RM, bool kExtras = true>
+// kExtras false: the launch has no log-sum-exp output or bitmask; kSample
+// false: no draw; that code is left out.
+template <int RM, bool kExtras = true, bool kSample = true>
 __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem& sm, FinalSmem& fs,
                                  uint32_t& last) {
   // every store of this thread has been acknowledged (gfx9 counts stores in vmcnt)
@@ -71,15 +71,16 @@ __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem
     bool have = false;
     if (kExtras && f.lse_part != nullptr) have = load_lse_pairs(f.lse_part + (size_t)m * n_part, n_part, pre);
     RowSample rs;
-    if (kExtras && f.smp.on) rs = load_row_sample(f.smp, m);
+    if (kSample && f.smp.on) rs = load_row_sample(f.smp, m);
     merge_final<RM>(f.cand + (size_t)m * n_in, n_in, f.heads + (size_t)m * f.n_chunks * kHeads,
                     f.n_chunks, f.kc, (uint32_t)f.k, f.values + (size_t)m * f.k,
                     f.indices + (size_t)m * f.k, (int)blockDim.x, sm, fs);
     lds_barrier();  // fs.out_* are complete; fs is reused by the next row
     float lse = 0.f;
     if (kExtras && f.lse_part != nullptr)
-      lse = merge_lse(f.lse_part + (size_t)m * n_part, n_part, f.lse ? f.lse + m : nullptr, sm, have, pre);
-    if (kExtras && f.smp.on) {
+      lse = merge_lse(f.lse_part + (size_t)m * n_part, n_part, f.lse ? f.lse + m : nullptr, sm, have,
+                      pre, kSample && f.smp.on);
+    if (kSample && f.smp.on) {
       sample_row(fs.out_bits, fs.out_idx, f.k, lse, rs, m, f.smp);
       lds_barrier();  // fs is reused by the next row
     }

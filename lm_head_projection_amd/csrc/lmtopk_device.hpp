@@ -907,7 +907,8 @@ __device__ __forceinline__ void merge_final(const uint2* in, int64_t n_in, const
 
 // Log-sum-exp of one row (Selective Log Softmax page, section "Kernel
 // design": per-slice maxima and sums of exponentials, combined), returned to
-// every thread and written to *out (unless out is null).  part[0, n)
+// every thread when `want` (else 0) and written to *out (unless out is
+// null).  part[0, n)
 // holds one (max, sum) pair per wave and chunk of the row, sum = the sum of
 // exp(logit - max) over that wave's rows (max -inf: no finite rows, sum 0;
 // max +inf: an +inf logit).  With M the largest max, the row's log-sum-exp
@@ -929,7 +930,8 @@ __device__ __forceinline__ bool load_lse_pairs(const uint2* part, int n, uint2 (
 }
 
 __device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out, SelectSmem& sm,
-                                          bool have, const uint2 (&pre)[kLsePairs]) {
+                                          bool have, const uint2 (&pre)[kLsePairs],
+                                          bool want = true) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
@@ -970,8 +972,11 @@ __device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out,
     sm.lse_out = r;
   }
   lds_barrier();
-  const float r = sm.lse_out;
-  lds_barrier();  // sm is reused
+  float r = 0.f;
+  if (want) {  // every thread reads the result (sm.lse_out), then sm may be reused
+    r = sm.lse_out;
+    lds_barrier();
+  }
   return r;
 }
 
