@@ -88,6 +88,12 @@ def parse_args():
     p.add_argument("--name", default="binary_v248320_h5120_k50_m1")
     p.add_argument("--summarize-trace", metavar="DIR")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    p.add_argument("--summarize-counters", metavar="DIR",
+                   help="turn a `rocprofv3 --pmc <SQ counters> GRBM_GUI_ACTIVE` run into "
+                        "profiles/<name>_counters.txt")
+    p.add_argument("--no-aux", action="store_true",
+                   help="skip the graph replay and single-copy measurements (for profiled runs: "
+                        "every scoring dispatch then reads rotated copies)")
     p.add_argument("--command", default="", help="command line recorded in a summary")
     return p.parse_args()
 
@@ -216,6 +222,48 @@ def summarize_pmc(fetch_dir, write_dir, name, command):
     print(f"wrote {base}.json/.txt")
 
 
+def summarize_counters(d, name, command):
+    """Per-dispatch medians of the SQ / GRBM counters of every kernel, and for
+    the scoring kernel the derived figures rocprof itself defines: VALU busy =
+    100 * sum(SQ_ACTIVE_INST_VALU) / CU_NUM / max(GRBM_GUI_ACTIVE), mean
+    occupancy = 400 * sum(SQ_WAVE_CYCLES) / max(GRBM_GUI_ACTIVE) / CU_NUM / 32
+    (percent of 32 waves per CU); CU_NUM = 256.  The per-dispatch
+    GRBM_GUI_ACTIVE of the CSV is the sum over the 8 XCDs, so its maximum
+    over them is taken as that sum / 8 (the XCDs run the dispatch together)."""
+    files, rows = _csv_rows(d, "counter_collection.csv")
+    if not rows:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    per = {}
+    for r in rows:
+        per.setdefault(r.get("Kernel_Name", "?"), {}).setdefault(r["Counter_Name"], []).append(
+            float(r["Counter_Value"]))
+    out = os.path.join(ROOT, "profiles", f"{name}_counters.txt")
+    cu = 256
+    with open(out, "w") as f:
+        f.write(f"rocprofv3 counters: {name}\n")
+        f.write(f"command: {command}\n")
+        f.write(f"kernel sources sha256[:16]: {kernel_source_hash()}\n\n")
+        for kern, cs in sorted(per.items(), key=lambda kv: SCORE_KERNEL not in kv[0]):
+            med = {c: statistics.median(v) for c, v in cs.items()}
+            n = max(len(v) for v in cs.values())
+            f.write(f"{kern[:120]}  ({n} dispatches, medians)\n")
+            for c in sorted(med):
+                f.write(f"  {c:24s} {med[c]:.6g}\n")
+            gui = med.get("GRBM_GUI_ACTIVE")
+            if gui:
+                gui /= 8.0  # one XCD's busy cycles
+                f.write(f"  busy cycles per XCD      {gui:.6g} ({gui / 2.4e3:.1f} us at 2.4 GHz)\n")
+                if "SQ_ACTIVE_INST_VALU" in med:
+                    f.write(f"  VALU busy                {100 * med['SQ_ACTIVE_INST_VALU'] / cu / gui:.1f} %\n")
+                if "SQ_WAVE_CYCLES" in med:
+                    f.write(f"  mean occupancy           {400 * med['SQ_WAVE_CYCLES'] / gui / cu / 32:.1f} % "
+                            f"of 32 waves per CU\n")
+            if med.get("SQ_WAVES") and "SQ_INSTS_VALU" in med:
+                f.write(f"  VALU instructions / wave {med['SQ_INSTS_VALU'] / med['SQ_WAVES']:.0f}\n")
+            f.write("\n")
+    print(f"wrote {out}")
+
+
 def load_traffic(name):
     fn = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(fn):
@@ -317,6 +365,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.name, args.command)
         return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.name, args.command)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -368,13 +419,15 @@ def main():
     # auxiliary measurements first (they also bring an idle GPU to its steady
     # clocks before the timed steps)
     aux_calls = max(args.steps, 1000)
-    graph_us = graph_replay_us(args, call, hip, stream, vals, idx)
-    # one packed copy only: served from the 256 MB Infinity Cache
-    warm_ms, _, _ = time_calls(hip, stream, lambda i, ev: call(i, ev, 1), aux_calls, False)
-    warm_us = warm_ms / aux_calls * 1e3
+    graph_us = warm_us = None
+    if not args.no_aux:
+        graph_us = graph_replay_us(args, call, hip, stream, vals, idx)
+        # one packed copy only: served from the 256 MB Infinity Cache
+        warm_ms, _, _ = time_calls(hip, stream, lambda i, ev: call(i, ev, 1), aux_calls, False)
+        warm_us = warm_ms / aux_calls * 1e3
     read_gbps = plain_read_gbps(hip, stream, dev)
     stream_gbps = plain_copy_gbps(hip, stream, dev)
-    log(f"hipGraph replay {graph_us} us/step; single-copy (cache) {warm_us:.2f} us/step; "
+    log(f"hipGraph replay {graph_us} us/step; single-copy (cache) {warm_us} us/step; "
         f"plain 1 GiB read {read_gbps:.0f} GB/s, copy {stream_gbps:.0f} GB/s (read + written)")
 
     for i in range(args.warmup):
@@ -441,8 +494,9 @@ def main():
         "graph_replay_us_per_step": graph_us,
         "plain_read_gbps_1gib": round(read_gbps, 1),
         "plain_copy_gbps_1gib": round(stream_gbps, 1),
-        "cache_served_single_copy": {"us_per_token": round(warm_us / M, 3),
-                                     "gbps": round(head_bytes / (warm_us * 1e-6) / 1e9, 1)},
+        "cache_served_single_copy": None if warm_us is None else {
+            "us_per_token": round(warm_us / M, 3),
+            "gbps": round(head_bytes / (warm_us * 1e-6) / 1e9, 1)},
     }
 
     if not args.no_compare:
