@@ -82,7 +82,7 @@ def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
             f"liblmtopk is not built ({_LIB_PATH} missing); run "
-            "`python -m lm_head_projection_amd.build` (needs hipcc for gfx950)")
+            "`python lm_head_projection_amd/build.py` (needs hipcc for gfx950)")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     psz = ctypes.POINTER(ctypes.c_size_t)

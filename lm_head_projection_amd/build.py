@@ -1,6 +1,6 @@
 """Build liblmtopk.so in-tree for gfx950.
 
-    python -m lm_head_projection_amd.build        # or lm_head_projection_amd.build.build()
+    python lm_head_projection_amd/build.py        # or lm_head_projection_amd.build.build()
 
 The HIP translation units (kernels + launchers, one per path) are compiled
 by hipcc for gfx950 in parallel; the C ABI layer is plain host C++ compiled
