@@ -85,7 +85,8 @@ def parse_args():
     p.add_argument("--cpu-reps", type=int, default=5, help="oracle calls timed for cpu_baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-compare", action="store_true", help="skip the materialized-logits comparison")
-    p.add_argument("--name", default="binary_v248320_h5120_k50_m1")
+    p.add_argument("--name", default="binary_v248320_h5120_k50_m1",
+                   help="summary name for the --summarize-* commands")
     p.add_argument("--summarize-trace", metavar="DIR")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     p.add_argument("--summarize-counters", metavar="DIR",
@@ -279,11 +280,23 @@ def load_traffic(name):
 # the benchmark
 # ---------------------------------------------------------------------------
 def algorithmic_score_bytes(M, V, H, k, bias, chunk_rows, lt):
+    """Packed head + bias + activations and scales read, plus the chunks'
+    candidate lists written (k entries of 8 bytes per row and chunk, with the
+    chunk count the library plans for these sizes)."""
     wq_b, ws_b = lt.packed_bytes(V, H)
-    C = chunk_rows or (1024 if V >= 1024 else -(-V // 64) * 64)
-    n_chunks = -(-V // C)
+    C, n_chunks, _ = lt.binary_plan(M, V, H, k, chunk_rows)
     kc = min(k, C)
     return wq_b + ws_b + (4 * V if bias else 0) + M * H + 4 * M + M * n_chunks * kc * 8
+
+
+def workload_name(args):
+    """Name of this workload's profile summaries (profiles/<name>_*)."""
+    n = f"binary_v{args.V}_h{args.H}_k{args.k}_m{args.M}"
+    n += "_bias" if args.bias else ""
+    n += "_lse" if args.lse else ""
+    n += "_sample" if args.sample else ""
+    n += f"_c{args.chunk_rows}" if args.chunk_rows else ""
+    return n
 
 
 def cpu_model():
@@ -460,7 +473,8 @@ def main():
     head_bytes = sum(lt.packed_bytes(V, H))
     alg_bytes = algorithmic_score_bytes(M, V, H, k, args.bias, args.chunk_rows, lt)
     achieved = alg_bytes / (score_us * 1e-6) / 1e9
-    traffic = load_traffic(args.name)
+    traffic = load_traffic(workload_name(args))  # null unless counters of this workload exist
+    plan_c, plan_n, plan_w = lt.binary_plan(M, V, H, k, args.chunk_rows)
 
     result = {
         "metric": METRIC,
@@ -481,7 +495,8 @@ def main():
                                f"{args.copies} rotated packed copies",
                    "V": V, "H": H, "k": k, "M": M, "bias": bool(args.bias), "lse": bool(args.lse),
                    "sample": bool(args.sample),
-                   "chunk_rows": args.chunk_rows or 1024, "rotated_copies": args.copies},
+                   "chunk_rows": plan_c, "chunks": plan_n, "waves_per_chunk": plan_w,
+                   "rotated_copies": args.copies},
         "gbps": round(head_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "head_bytes": head_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,

@@ -223,6 +223,19 @@ lmtopk_status lmtopk_packed_bytes(int64_t V, int64_t H, int32_t group_size,
 lmtopk_status lmtopk_workspace_bytes(int64_t M, int64_t V, int32_t k,
                                      const lmtopk_options* opt, size_t* bytes);
 
+/* Host-only: the chunking lmtopk_binary uses for these sizes and options:
+   vocabulary rows per chunk (one workgroup scores and selects one chunk),
+   the number of chunks, and the waves of a chunk workgroup.  With
+   chunk_rows 0 the library takes 1,024-row chunks, or, when at most 128 of
+   them would cover V (leaving CUs idle) and the final merge can still run in
+   the chunk launch, 512-row chunks scored by two waves per 64-row tile (one
+   per half of the groups; also for any chunk of up to 512 rows where the
+   LDS allows).  The values never change a result.
+   Errors: NULL, SHAPE, K, GROUP, OPTIONS. */
+lmtopk_status lmtopk_binary_plan(int64_t M, int64_t V, int64_t H, int32_t k,
+                                 const lmtopk_options* opt, int32_t* chunk_rows,
+                                 int32_t* n_chunks, int32_t* waves);
+
 /* Zero-fill a workspace of `bytes` bytes (device pointer, 16-byte aligned)
    on `stream`, with a kernel rather than a memset so that the call may be
    captured into a graph.  Needed once per new workspace (see the
@@ -252,11 +265,15 @@ lmtopk_status lmtopk_pack_binary(const void* w, lmtopk_dtype w_dtype, int64_t V,
  *   bias      : [V] fp32 or NULL.
  *   values    : out [M, k] fp32;  indices : out [M, k] int64.
  *   workspace : lmtopk_workspace_bytes(M, V, k, opt) bytes, device.
- * Logit of row m, entry v:
+ * Logit of row m, entry v (G = H / 128 groups, Q = ceil(G / 4) quads of
+ * groups, Gh = 4 * floor(Q / 2)):
  *   D_g = sum over the 128 j of group g of act_q[m, j] * sign[v, j]  (exact)
- *   acc = fp32 fused multiply-add chain over g = 0, 1, ..., G-1 of
+ *   lo  = fp32 fused multiply-add chain over g = 0, 1, ..., Gh-1 of
  *         (float)D_g * wscale[v, g], starting from 0
- *   L   = fmaf(acc, act_scale[m], bias ? bias[v] : 0)
+ *   hi  = the same chain over g = Gh, ..., G-1, starting from 0
+ *   L   = fmaf(lo + hi, act_scale[m], bias ? bias[v] : 0)
+ * (the same operations for every chunk size, M and option, so a row's
+ * logits never depend on them)
  * Errors: NULL, SHAPE (also M * H > LMTOPK_MAX_BINARY_MH), K, GROUP, ALIGN,
  * WORKSPACE, OPTIONS (also chunk_rows 2048 with M > 2), HIP.
  */

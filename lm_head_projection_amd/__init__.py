@@ -32,6 +32,7 @@ __all__ = [
     "layout_version",
     "packed_bytes",
     "workspace_bytes",
+    "binary_plan",
     "pack_binary",
     "lm_head_topk_binary",
     "lm_head_topk_dense",
@@ -86,12 +87,14 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
     psz = ctypes.POINTER(ctypes.c_size_t)
+    pi32 = ctypes.POINTER(ctypes.c_int32)
     popt = ctypes.POINTER(_Options)
     sig = {
         "lmtopk_layout_version": ([], i32),
         "lmtopk_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "lmtopk_packed_bytes": ([i64, i64, i32, psz, psz], ctypes.c_int),
         "lmtopk_workspace_bytes": ([i64, i64, i32, popt, psz], ctypes.c_int),
+        "lmtopk_binary_plan": ([i64, i64, i64, i32, popt, pi32, pi32, pi32], ctypes.c_int),
         "lmtopk_workspace_init": ([vp, sz, vp], ctypes.c_int),
         "lmtopk_pack_binary": ([vp, ctypes.c_int, i64, i64, i32, vp, vp, vp], ctypes.c_int),
         "lmtopk_binary": ([vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp, vp, sz, popt, vp],
@@ -245,6 +248,17 @@ def workspace_bytes(M, V, k, chunk_rows=0):
     o = _opts(chunk_rows)
     _check(_lib.lmtopk_workspace_bytes(M, V, k, ctypes.byref(o), ctypes.byref(n)))
     return n.value
+
+
+@functools.lru_cache(maxsize=256)
+def binary_plan(M, V, H, k, chunk_rows=0):
+    """(chunk_rows, n_chunks, waves per chunk workgroup) that lm_head_topk_binary
+    uses for these sizes; they never change a result."""
+    c, n, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    o = _opts(chunk_rows)
+    _check(_lib.lmtopk_binary_plan(M, V, H, k, ctypes.byref(o), ctypes.byref(c), ctypes.byref(n),
+                                   ctypes.byref(w)))
+    return c.value, n.value, w.value
 
 
 def _stream(t):

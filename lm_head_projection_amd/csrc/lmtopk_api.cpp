@@ -40,7 +40,8 @@ lmtopk_status hip_status(int e) { return e == 0 ? LMTOPK_OK : LMTOPK_ERR_HIP; }
 
 }  // namespace
 
-int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, Geometry* g) {
+int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, int split_ok,
+                  Geometry* g) {
   int st = check_mvk(M, V, k);
   if (st) return st;
   memset(g, 0, sizeof(*g));
@@ -50,14 +51,24 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, Geome
   g->n_tiles = (V + 63) / 64;
   int C = chunk_rows_opt;
   if (C == 0) {
-    // one 1024-row chunk per workgroup; small vocabularies use one chunk
+    // one 1024-row chunk per workgroup; small vocabularies use one chunk.
+    // Up to 128 such chunks leave at least half of the 256 CUs idle: with
+    // two waves per tile a 512-row chunk still has 16 waves, so twice the
+    // workgroups stream the head (if the fused merge still holds their
+    // candidates).
     C = V >= 1024 ? 1024 : (int)(g->n_tiles * 64);
+    const int64_t n512 = (V + 511) / 512;
+    if (split_ok && V >= 1024 && (V + 1023) / 1024 <= 128 &&
+        n512 * (k < 512 ? k : 512) <= 1024 * kFusedSlots)
+      C = 512;
   }
   g->chunk_rows = C;
   // rows per lane: 1 for chunks of up to 1024 rows (up to 16 waves); a
-  // 2048-row chunk is 8 waves of 4 rows per lane
+  // 2048-row chunk is 8 waves of 4 rows per lane.  Chunks of up to 512 rows
+  // take two waves per tile where the caller can.
   g->rpl = C <= 1024 ? 1 : 4;
-  g->nw = C / (64 * g->rpl);
+  g->ks = split_ok && C <= 512 ? 2 : 1;
+  g->nw = g->ks * C / (64 * g->rpl);
   g->n_chunks = (int)((V + C - 1) / C);
   g->kc = k < C ? k : C;
   const int64_t n0 = (int64_t)g->n_chunks * g->kc;
@@ -151,10 +162,15 @@ lmtopk_status lmtopk_workspace_bytes(int64_t M, int64_t V, int32_t k, const lmto
   if (!bytes) return LMTOPK_ERR_NULL;
   int st = lmtopk::check_options(opt);
   if (st) return (lmtopk_status)st;
-  Geometry g;
-  st = lmtopk::make_geometry(M, V, k, opt ? opt->chunk_rows : 0, &g);
-  if (st) return (lmtopk_status)st;
-  *bytes = g.workspace_bytes;
+  // every path's plan: with and without two waves per tile
+  size_t need = 0;
+  for (int split_ok = 0; split_ok < 2; ++split_ok) {
+    Geometry g;
+    st = lmtopk::make_geometry(M, V, k, opt ? opt->chunk_rows : 0, split_ok, &g);
+    if (st) return (lmtopk_status)st;
+    if (g.workspace_bytes > need) need = g.workspace_bytes;
+  }
+  *bytes = need;
   return LMTOPK_OK;
 }
 
@@ -209,11 +225,11 @@ static lmtopk_status sampling_checks(const lmtopk_sampling* sp, int32_t k, Geome
 
 static lmtopk_status common_checks(const void* workspace, size_t workspace_bytes, float* values,
                                    int64_t* indices, const lmtopk_options* opt, int64_t M,
-                                   int64_t V, int32_t k, Geometry* g) {
+                                   int64_t V, int32_t k, int split_ok, Geometry* g) {
   if (!values || !indices) return LMTOPK_ERR_NULL;
   int st = lmtopk::check_options(opt);
   if (st) return (lmtopk_status)st;
-  st = lmtopk::make_geometry(M, V, k, opt ? opt->chunk_rows : 0, g);
+  st = lmtopk::make_geometry(M, V, k, opt ? opt->chunk_rows : 0, split_ok, g);
   if (st) return (lmtopk_status)st;
   if (!lmtopk::aligned16(values) || !lmtopk::aligned16(indices)) return LMTOPK_ERR_ALIGN;
   g->lse = opt ? opt->lse : nullptr;
@@ -237,6 +253,30 @@ static void* const* score_events(const lmtopk_options* opt) {
   return opt ? static_cast<void* const*>(opt->score_events) : nullptr;
 }
 
+// Two waves per tile for the binary path where their exchange area fits
+// gfx950's LDS (M and H are checked elsewhere; any value here is safe).
+static int binary_split_ok(int64_t M, int64_t H) {
+  return H >= 1 && M >= 1 && M <= LMTOPK_MAX_ROWS && H <= LMTOPK_MAX_BINARY_MH &&
+         lmtopk::binary_lds_bytes(M, H, 2) + lmtopk::kChunkStaticLds <= lmtopk::kLdsPerBlock;
+}
+
+lmtopk_status lmtopk_binary_plan(int64_t M, int64_t V, int64_t H, int32_t k,
+                                 const lmtopk_options* opt, int32_t* chunk_rows,
+                                 int32_t* n_chunks, int32_t* waves) {
+  if (!chunk_rows || !n_chunks || !waves) return LMTOPK_ERR_NULL;
+  int st = lmtopk::check_options(opt);
+  if (st) return (lmtopk_status)st;
+  if (H < 1) return LMTOPK_ERR_SHAPE;
+  if (H % LMTOPK_GROUP_SIZE != 0) return LMTOPK_ERR_GROUP;
+  Geometry g;
+  st = lmtopk::make_geometry(M, V, k, opt ? opt->chunk_rows : 0, binary_split_ok(M, H), &g);
+  if (st) return (lmtopk_status)st;
+  *chunk_rows = g.chunk_rows;
+  *n_chunks = g.n_chunks;
+  *waves = g.nw;
+  return LMTOPK_OK;
+}
+
 // The binary call in two phases: every argument check (the workspace only
 // as a size and an alignment), then the launches.  lmtopk_binary and
 // lmtopk_binary_noalloc share both.
@@ -246,7 +286,8 @@ static lmtopk_status binary_checks(const int8_t* act_q, const float* act_scale, 
                                    int64_t* indices, const void* workspace,
                                    size_t workspace_bytes, const lmtopk_options* opt, Geometry* g) {
   if (!act_q || !act_scale || !wq || !wscale) return LMTOPK_ERR_NULL;
-  lmtopk_status st = common_checks(workspace, workspace_bytes, values, indices, opt, M, V, k, g);
+  lmtopk_status st = common_checks(workspace, workspace_bytes, values, indices, opt, M, V, k,
+                                   binary_split_ok(M, H), g);
   if (st) return st;
   if (H < 1) return LMTOPK_ERR_SHAPE;
   if (group_size != LMTOPK_GROUP_SIZE || H % LMTOPK_GROUP_SIZE != 0) return LMTOPK_ERR_GROUP;
@@ -257,7 +298,8 @@ static lmtopk_status binary_checks(const int8_t* act_q, const float* act_scale, 
     return LMTOPK_ERR_ALIGN;
   size_t lds_max = 0;
   if (lmtopk::max_lds_per_block(&lds_max)) return LMTOPK_ERR_HIP;
-  if (lmtopk::binary_lds_bytes(M, H) + lmtopk::kChunkStaticLds > lds_max) return LMTOPK_ERR_SHAPE;
+  if (lmtopk::binary_lds_bytes(M, H, g->ks) + lmtopk::kChunkStaticLds > lds_max)
+    return LMTOPK_ERR_SHAPE;
   return LMTOPK_OK;
 }
 
@@ -309,7 +351,7 @@ lmtopk_status lmtopk_dense(const void* hidden, const void* weight, lmtopk_dtype 
   if (!hidden || !weight) return LMTOPK_ERR_NULL;
   Geometry g;
   lmtopk_status st =
-      common_checks(workspace, workspace_bytes, values, indices, opt, M, V, k, &g);
+      common_checks(workspace, workspace_bytes, values, indices, opt, M, V, k, 0, &g);
   if (st) return st;
   if (H < 1) return LMTOPK_ERR_SHAPE;
   if (dtype != LMTOPK_F32 && dtype != LMTOPK_BF16) return LMTOPK_ERR_DTYPE;
@@ -332,7 +374,7 @@ lmtopk_status lmtopk_select(const float* logits, int64_t M, int64_t V, int64_t l
   if (!logits) return LMTOPK_ERR_NULL;
   Geometry g;
   lmtopk_status st =
-      common_checks(workspace, workspace_bytes, values, indices, opt, M, V, k, &g);
+      common_checks(workspace, workspace_bytes, values, indices, opt, M, V, k, 0, &g);
   if (st) return st;
   if (ld < V) return LMTOPK_ERR_SHAPE;
   if (!lmtopk::aligned16(logits)) return LMTOPK_ERR_ALIGN;

@@ -38,6 +38,7 @@ struct BinaryArgs {
   int64_t V, H, n_tiles;
   int G, Q;
   int tiles_per_chunk;
+  int ks;  // waves per tile: 1, or 2 (a pair of waves splits the groups)
   ChunkOut out;
 };
 
@@ -91,9 +92,21 @@ __device__ __forceinline__ void spread_signs(uint32_t w0, uint32_t w1, uint32_t 
 
 // Lane l of wave w owns the R rows ((chunk * tiles_per_chunk + w * R + r) * 64 + l),
 // r < R, and scores them together.  Each group's 128 sign bits of a row are
-// one 16-byte load; the four scales of a quad of groups are one more.  The
-// fp32 logit accumulates fmaf((float)D_g, scale_g, acc) in ascending g, so
-// every row takes the same operation sequence wherever it sits.
+// one 16-byte load; the four scales of a quad of groups are one more.
+//
+// Accumulation order (the same on every path, so a row's logit does not
+// depend on the chunk size or on M): with Q = ceil(G / 4) quads and
+// Qh = floor(Q / 2), the quads [0, Qh) and [Qh, Q) are two chains, each
+// accumulating fmaf((float)D_g, scale_g, acc) from 0 in ascending g, and the
+// logit's dot part is lo + hi.
+//
+// Two waves per tile (ks = 2, chunks of up to 512 rows, one row per lane):
+// waves 2t and 2t + 1 share tile t, the first running the chain of [0, Qh)
+// and the second that of [Qh, Q) for all 64 rows, so a workgroup of 16
+// waves streams a 512-row chunk.  The first then keeps rows 0-31 of the
+// tile and the second rows 32-63; each leaves the partial sums of the rows
+// it gives up in LDS for the other.  Without a split (ks = 1) one wave runs
+// both chains.
 //
 // Latency: the activation bytes are requested first and the first two quads
 // of weights right after them; the bit planes are built while those weights
@@ -106,6 +119,8 @@ static_assert(sizeof(SelectSmem) + sizeof(ChunkSmem) + 16 <= kChunkStaticLds,
 
 // Quads of weight loads in flight per wave.
 constexpr int kQuadBuffers = 2;
+// Waves of a chunk workgroup with two waves per tile (512-row chunks).
+constexpr int kPairWaves = 16;
 
 // kExtras: a log-sum-exp output or a bitmask; kSample (implies kExtras): a
 // token draw.  Calls without them run instances with that code left out.
@@ -123,12 +138,24 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   const int G = a.G;
   PlaneGroup* pgs = reinterpret_cast<PlaneGroup*>(dyn_lds);          // [M][G]
   int* cg = reinterpret_cast<int*>(pgs + (size_t)M * G);              // [M][G] C of the group
+  float* xch = reinterpret_cast<float*>(cg + (size_t)M * G);          // ks = 2: [waves][32][M]
+  uint32_t* xflag = reinterpret_cast<uint32_t*>(xch + (size_t)kPairWaves * 32 * M);  // [waves]
   const int lane = lane_id();
   const int wave = wave_id();
   const int nw = blockDim.x >> 6;
   const int Qf = G >> 2;  // full quads
-  const int64_t tile0 = (int64_t)blockIdx.x * a.tiles_per_chunk + (int64_t)wave * R;
+  const bool pair = R == 1 && a.ks == 2;
+  const bool second = pair && (wave & 1);  // runs the second chain of a pair
+  const int64_t tile0 =
+      (int64_t)blockIdx.x * a.tiles_per_chunk + (int64_t)(pair ? wave >> 1 : wave * R);
   const bool active = tile0 < a.n_tiles;
+  // this wave's quads [qa, qb); `split`: the quad after which a wave that
+  // runs both chains starts the second (-1: it runs one)
+  const int Qh = a.Q >> 1;
+  const int qa = second ? Qh : 0;
+  const int qb = pair && !second ? Qh : a.Q;
+  const int split = pair ? -1 : Qh;
+  if (pair && threadIdx.x < kPairWaves) xflag[threadIdx.x] = 0u;  // ordered by the barrier below
 
   // a tile past the last one reads the last tile; its rows are never offered
   const uint4* wp[R];
@@ -236,13 +263,13 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   float4 sbuf[kQuadBuffers][R];
 #pragma unroll
   for (int b = 0; b < kQuadBuffers; ++b) {
-    const int qc = b < a.Q ? b : a.Q - 1;
+    const int qc = qa + b < a.Q ? qa + b : a.Q - 1;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       sbuf[b][r] = ld_stream(&sp[r][qc * 64]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int g = 4 * b + i;
+        const int g = 4 * (qa + b) + i;
         buf[b][r][i] = ld_stream(&wp[r][(g < G ? g : G - 1) * 64]);
       }
     }
@@ -253,11 +280,22 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   build_masks(wave, x0, x1);
   lds_barrier();
 
-  float acc[R][M];
+  float acc[R][M], lo[R][M];  // running chain; the finished first chain
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+    for (int m = 0; m < M; ++m) acc[r][m] = lo[r][m] = 0.f;
+  auto after_quad = [&](int qq) {  // a wave running both chains starts the second
+    if (qq + 1 == split) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          lo[r][m] = acc[r][m];
+          acc[r][m] = 0.f;
+        }
+    }
+  };
 
   auto compute_group = [&](int g, const uint4 (&w)[R], const float (&s)[R]) {
     if constexpr (kBytes) {
@@ -322,11 +360,13 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     // quads q .. q + kQuadBuffers - 1 are in flight at the top; each buffer is
     // refilled right after its last use
     constexpr int NB = kQuadBuffers;
-    int q = 0;
-    for (; q + 2 * NB - 1 < Qf; q += NB) {
+    const int qe = qb < Qf ? qb : Qf;  // end of this wave's full quads
+    int q = qa;
+    for (; q + 2 * NB - 1 < qe; q += NB) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         compute_quad(q + b, buf[b], sbuf[b]);
+        after_quad(q + b);
         __builtin_amdgcn_sched_barrier(0);
         load_quad(q + b + NB, buf[b], sbuf[b]);
         __builtin_amdgcn_sched_barrier(0);
@@ -335,15 +375,19 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     // drain: fewer than 2 * NB quads remain
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      if (q + b < Qf) {
+      if (q + b < qe) {
         compute_quad(q + b, buf[b], sbuf[b]);
-        if (q + b + NB < Qf) load_quad(q + b + NB, buf[b], sbuf[b]);
+        after_quad(q + b);
+        if (q + b + NB < qe) load_quad(q + b + NB, buf[b], sbuf[b]);
       }
     }
 #pragma unroll
     for (int b = 0; b < NB; ++b)
-      if (q + NB + b < Qf) compute_quad(q + NB + b, buf[b], sbuf[b]);
-    if (4 * Qf < G) {  // last, partial quad
+      if (q + NB + b < qe) {
+        compute_quad(q + NB + b, buf[b], sbuf[b]);
+        after_quad(q + NB + b);
+      }
+    if (qb > Qf) {  // last, partial quad (always in the second chain)
       float4 st[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) st[r] = ld_stream(&sp[r][Qf * 64]);
@@ -360,13 +404,45 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     }
   }
 
+  if (pair) {
+    // each wave of the pair leaves its partial sums of the rows it gives up
+    // (the other half of the lanes) in its LDS slot and raises its flag, then
+    // takes the partner's; both write before they wait, so the wait ends
+    // (bounded all the same)
+    const bool keep = (lane < 32) != second;
+    float* mine = xch + (size_t)wave * 32 * M + (lane & 31) * M;
+    if (!keep) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) mine[m] = acc[0][m];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (lane == 0) *(volatile lds_t<uint32_t>*)&xflag[wave] = 1u;
+    for (int spin = 0; spin < kThresholdSpinMax; ++spin) {
+      if (uniform(*(volatile lds_t<uint32_t>*)&xflag[wave ^ 1])) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    const float* theirs = xch + (size_t)(wave ^ 1) * 32 * M + (lane & 31) * M;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float t = theirs[m];
+      lo[0][m] = second ? t : acc[0][m];
+      acc[0][m] = second ? acc[0][m] : t;
+    }
+  }
+  // the dot part: first chain + second chain
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = lo[r][m] + acc[r][m];
+
   int32_t idx[R];
   uint32_t valid = 0u;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t v = (tile0 + r) * 64 + lane;
     idx[r] = (int32_t)v;
-    const bool vv = (tile0 + r) < a.n_tiles && v < a.V;
+    const bool vv = (tile0 + r) < a.n_tiles && v < a.V && (!pair || (lane < 32) != second);
     valid |= (vv ? 1u : 0u) << r;
     if (a.bias == nullptr || !vv) bias_v[r] = 0.f;
   }
@@ -423,9 +499,10 @@ void (*binary_kernel(int M, int rpl, int mode))(BinaryArgs) {
 }
 }  // namespace
 
-size_t binary_lds_bytes(int64_t M, int64_t H) {
+size_t binary_lds_bytes(int64_t M, int64_t H, int ks) {
   const int64_t G = H / kGroup;
-  return (size_t)(M * G * sizeof(PlaneGroup) + M * G * 4);
+  const int64_t pair = ks == 2 ? (int64_t)kPairWaves * (32 * M * 4 + 4) : 0;
+  return (size_t)(M * G * sizeof(PlaneGroup) + M * G * 4 + pair);
 }
 int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* act_scale,
                          const void* wq, const float* wscale, const float* bias, int64_t H,
@@ -443,11 +520,12 @@ int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* ac
   a.G = (int)(H / kGroup);
   a.Q = (a.G + 3) / 4;
   a.tiles_per_chunk = g.chunk_rows / 64;
+  a.ks = g.ks;
   a.out = chunk_out(g, workspace, values, indices);
   const int mode = g.smp.on ? 2 : (g.lse != nullptr || g.allowed != nullptr) ? 1 : 0;
   auto kern = binary_kernel((int)g.M, g.rpl, mode);
   if (!kern) return (int)hipErrorInvalidValue;
-  return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), binary_lds_bytes(g.M, H), stream, a,
-                      events);
+  return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw), binary_lds_bytes(g.M, H, g.ks),
+                      stream, a, events);
 }
 }  // namespace lmtopk

@@ -45,7 +45,9 @@ struct Geometry {
   int64_t M, V;
   int k;
   int chunk_rows;  // C: vocabulary rows per chunk (workgroup)
-  int rpl;         // rows per lane: C = 64 * nw * rpl
+  int rpl;         // rows per lane
+  int ks;          // waves per 64-row tile: 1, or 2 (binary path: each wave
+                   // scores half of the groups); C * ks = 64 * nw * rpl
   int nw;          // waves per chunk workgroup
   int n_chunks;
   int kc;          // candidate slots per chunk per row = min(k, C)
@@ -64,8 +66,12 @@ struct Geometry {
   SampleParams smp;        // this call's draw (not part of the plan)
 };
 
-// Returns 0 or an lmtopk_status code (SHAPE, K, OPTIONS).
-int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, Geometry* g);
+// Returns 0 or an lmtopk_status code (SHAPE, K, OPTIONS).  split_ok: the
+// caller's chunk kernel can score a tile with two waves (the binary path,
+// when its LDS allows); the automatic chunk size and the waves per chunk
+// then take it into account.
+int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, int split_ok,
+                  Geometry* g);
 
 // Launchers; each returns a hipError_t value (0 = success).  `events` of the
 // chunk launchers: null, or two hipEvent_t recording the kernel's start and end.
@@ -102,8 +108,12 @@ int max_lds_per_block(size_t* bytes);
 // and the head staging); the dynamic LDS comes on top.
 constexpr size_t kChunkStaticLds = 57344;
 
-// LDS bytes the scoring kernels need.
-size_t binary_lds_bytes(int64_t M, int64_t H);
+// LDS per workgroup of gfx950 (the split decision is made from it, so that
+// it does not need a device; the launch checks the device's own limit).
+constexpr size_t kLdsPerBlock = 163840;
+
+// LDS bytes the scoring kernels need; ks = waves per tile.
+size_t binary_lds_bytes(int64_t M, int64_t H, int ks);
 size_t dense_lds_bytes(int64_t M, int chunk_rows);
 
 }  // namespace lmtopk

@@ -178,3 +178,53 @@ def check_draw(r, gpu_token, gpu_kept, top_k, top_p, min_p, k, eps_z=0.0, tol_p=
     assert score[pos] >= score[best] - (bound[pos] + bound[best]), \
         f"token {int(gpu_token)} (score {score[pos]!r}) vs best {idx[best]} ({score[best]!r})"
     return int(gpu_token) != r["token"] or n != r["kept"]
+
+
+# ---------------------------------------------------------------------------
+# The binary path's documented fp32 operation order, evaluated exactly: each
+# fused multiply-add and addition is the exact rational result rounded once
+# to fp32 (round to nearest, ties to even).  Used on a few sampled logits to
+# check that the kernels follow the order the header states, bit for bit.
+# ---------------------------------------------------------------------------
+from fractions import Fraction
+
+
+def round_f32(x):
+    """Exact rational x rounded to the nearest fp32 (ties to even); normal
+    range only (the sampled logits are far from under- and overflow)."""
+    if x == 0:
+        return 0.0
+    neg = x < 0
+    x = -x if neg else x
+    e = x.numerator.bit_length() - x.denominator.bit_length() - 24
+    scale = lambda e: Fraction(2) ** e
+    while x / scale(e) >= 2 ** 24:
+        e += 1
+    while x / scale(e) < 2 ** 23:
+        e -= 1
+    q = x / scale(e)
+    n = q.numerator // q.denominator
+    r = q - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = float(n * scale(e))
+    return -v if neg else v
+
+
+def binary_logit_f32(D, scales, act_scale, bias):
+    """L = fmaf(lo + hi, act_scale, bias) with lo, hi the fp32 fused
+    multiply-add chains of (float)D_g * scale_g over g < Gh and g >= Gh,
+    Gh = 4 * floor(ceil(G / 4) / 2).  D: exact integer group dots [G];
+    scales: fp32 [G]."""
+    G = len(D)
+    Gh = 4 * (((G + 3) // 4) // 2)
+
+    def chain(gs):
+        acc = 0.0
+        for g in gs:
+            acc = round_f32(Fraction(float(np.float32(D[g]))) * Fraction(float(scales[g])) + Fraction(acc))
+        return acc
+
+    lo, hi = chain(range(Gh)), chain(range(Gh, G))
+    s = round_f32(Fraction(lo) + Fraction(hi))
+    return round_f32(Fraction(s) * Fraction(float(act_scale)) + Fraction(float(bias)))

@@ -56,6 +56,40 @@ def test_layout_and_sizes():
                                                    + 8 * 16 * 1024 * 8 + 8 * 243 * 16 * 8)
 
 
+def test_workspace_covers_the_two_wave_plan():
+    # V = 128,256: 126 chunks of 1,024 rows would leave half of the CUs idle,
+    # so the binary path scores 251 chunks of 512 rows with two waves per tile
+    # (16 waves per chunk); the size query covers that plan as well as the
+    # other paths' 126 chunks
+    split = 256 + 8192 + 100608 + 32256      # 251 x 4 x 8 -> 8,192; 251 x 50 x 8 -> 100,608;
+    plain = 256 + 4096 + 50432 + 16128       # 251 x 16 x 8 -> 32,256 (vs 126 chunks)
+    assert lt.workspace_bytes(1, 128256, 50) == max(split, plain) == split
+    kw = dict(V=128256, H=4096, k=50)
+    assert _binary(**kw, ws_bytes=split - 1) == WORKSPACE
+    assert _binary(**kw, ws_bytes=split) == HIP  # every host check passed; no device here
+    assert _dense(**kw, M=1, ws_bytes=plain - 1) == WORKSPACE
+    assert _dense(**kw, M=1, ws_bytes=plain) == HIP
+    # the plan the binary path reports: 251 chunks of 512 rows, 16 waves each;
+    # explicit sizes up to 512 rows take two waves per tile as well
+    assert lt.binary_plan(1, 128256, 4096, 50) == (512, 251, 16)
+    assert lt.binary_plan(1, 128256, 4096, 50, chunk_rows=256) == (256, 501, 8)
+    assert lt.binary_plan(1, 128256, 4096, 50, chunk_rows=1024) == (1024, 126, 16)
+    assert lt.binary_plan(1, 248320, 5120, 50) == (1024, 243, 16)
+    assert lt.binary_plan(2, 248320, 5120, 50, chunk_rows=2048) == (2048, 122, 8)
+    assert lt.binary_plan(1, 40, 128, 40) == (64, 1, 2)
+    # the largest activation block (M * H = 65,536) still fits the exchange area
+    assert lt.binary_plan(8, 5000, 8192, 50) == (512, 10, 16)
+    lib = lt._lib
+    c = ctypes.c_int32()
+    assert lib.lmtopk_binary_plan(1, 1000, 200, 5, None, ctypes.byref(c), ctypes.byref(c),
+                                  ctypes.byref(c)) == GROUP
+    assert lib.lmtopk_binary_plan(1, 1000, 256, 5, None, None, ctypes.byref(c),
+                                  ctypes.byref(c)) == NULL
+    # a large k keeps 1,024-row chunks (the fused merge could not hold 251 x 512
+    # candidates), so both plans coincide
+    assert lt.workspace_bytes(1, 128256, 512) == lt.workspace_bytes(1, 128256, 512, chunk_rows=1024)
+
+
 def test_status_strings():
     lib = lt._lib
     for s in range(10):

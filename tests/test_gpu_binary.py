@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synthetic
-from parity import binary_eps_fn, compare_end_to_end
+from parity import binary_eps_fn, binary_logit_f32, compare_end_to_end
 
 pytestmark = pytest.mark.gpu
 
@@ -221,7 +221,7 @@ def test_cfg2_invariants(cfg2):
     for _ in range(10):  # repeated calls are bitwise identical
         v, i = cfg2.run(50)
         assert torch.equal(i, i0) and torch.equal(v.view(torch.int32), v0.view(torch.int32))
-    for C in (64, 256, 512, 2048):  # chunk size does not change a bit
+    for C in (64, 256, 512, 1024, 2048):  # chunk size does not change a bit
         v, i = cfg2.run(50, chunk_rows=C)
         assert torch.equal(i, i0) and torch.equal(v.view(torch.int32), v0.view(torch.int32))
     for m in range(2):  # a row alone equals the same row inside M=2
@@ -263,6 +263,7 @@ def flagship():
 def test_cfg4_flagship_m1(flagship):
     v, i, relaxed = flagship.check(50, rows=[0])
     assert relaxed <= 2
+    assert_documented_fp32_order(flagship, v, i, [0])
 
 
 @pytest.mark.slow
@@ -283,7 +284,8 @@ def test_cfg5_sweep_with_bias(flagship, M, k):
 # ---------------------------------------------------------------------------
 # chunk sizes x optional outputs: every binary kernel instance that exists
 # runs (2048-row chunks, four rows per lane, serve M <= 2; from three rows on
-# the library refuses them)
+# the library refuses them), with one wave per tile (1,024 and 2,048 rows)
+# and with two (up to 512 rows; the automatic size at V = 20,001)
 # ---------------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def wide_case():
@@ -299,7 +301,7 @@ def _mask(M, V, seed):
 
 
 @pytest.mark.parametrize("extras", ["none", "lse_and_mask"])
-@pytest.mark.parametrize("chunk_rows", [0, 2048])
+@pytest.mark.parametrize("chunk_rows", [0, 1024, 2048])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 8])
 def test_chunk_sizes_and_extras(wide_case, M, chunk_rows, extras):
     c, k = wide_case, 50
@@ -326,3 +328,45 @@ def test_chunk_sizes_and_extras(wide_case, M, chunk_rows, extras):
     # the chunk size does not change a bit
     v0, i0 = lt.lm_head_topk_binary(aq, sc, c.wq, c.ws, **{**kw, "chunk_rows": 256})
     assert torch.equal(i0, i) and torch.equal(v0.view(torch.int32), v.view(torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# the two accumulation chains (quads [0, Qh) and [Qh, Q), Qh = floor(Q / 2)):
+# one wave running both (1,024 and 2,048-row chunks) and two waves sharing a
+# tile (512 and 64-row chunks) give the same bits for every group count,
+# including an empty first chain (G <= 3) and a partial last quad
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 7, 8, 9, 12, 13])
+@pytest.mark.parametrize("M", [1, 2, 5])
+def test_split_chains_bitwise_across_chunk_sizes(M, G):
+    c = Case(M, 128 * G, 3001, seed=G, with_bias=True)
+    v0, i0, _ = c.check(20, chunk_rows=1024)
+    sizes = (512, 64, 2048) if M <= 2 else (512, 64)
+    for C in sizes:
+        v, i = c.run(20, chunk_rows=C)
+        assert torch.equal(i, i0) and torch.equal(v.view(torch.int32), v0.view(torch.int32)), C
+
+
+def assert_documented_fp32_order(c, v, i, rows, n=None):
+    """The returned values are the header's fp32 formula (two fused
+    multiply-add chains over the group dots, their sum, then the row scale
+    and bias), evaluated exactly with one rounding per operation: bit for
+    bit, on the first n entries of each row."""
+    v, i = v.cpu().numpy(), i.cpu().numpy()
+    for r, m in enumerate(rows):
+        a = c.act_q[m].astype(np.int64).reshape(c.G, 128)
+        for j in range(i.shape[1] if n is None else n):
+            ix = int(i[r, j])
+            D = (a * c.signs[ix].astype(np.int64).reshape(c.G, 128)).sum(axis=1)
+            b = 0.0 if c.bias is None else float(c.bias[ix])
+            want = np.float32(binary_logit_f32(D, c.scales[ix], c.act_scale[m], b))
+            got = np.float32(v[r, j])
+            assert got.view(np.uint32) == want.view(np.uint32), (m, j, ix, got, want)
+
+
+@pytest.mark.parametrize("M,G,C", [(1, 5, 0), (2, 40, 1024), (2, 3, 2048), (5, 13, 512),
+                                   (8, 8, 0), (3, 32, 64)])
+def test_logits_follow_the_documented_fp32_order(M, G, C):
+    c = Case(M, 128 * G, 3001, seed=100 + G, with_bias=True)
+    v, i = c.run(12, chunk_rows=C)
+    assert_documented_fp32_order(c, v, i, list(range(M)))
