@@ -284,12 +284,13 @@ def test_cfg5_sweep_with_bias(flagship, M, k):
 # ---------------------------------------------------------------------------
 # chunk sizes x optional outputs: every binary kernel instance that exists
 # runs (2048-row chunks, four rows per lane, serve M <= 2; from three rows on
-# the library refuses them), with one wave per tile (1,024 and 2,048 rows)
-# and with two (up to 512 rows; the automatic size at V = 20,001)
+# the library refuses them), with one wave per tile (1,024 and 2,048 rows;
+# at 1,024 rows and M = 4 the tiles' second chains are shared out as tasks) and
+# with two (up to 512 rows; the automatic size at V = 20,001)
 # ---------------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def wide_case():
-    return Case(8, 1024, 20001, seed=9, with_bias=True)
+    return Case(8, 2048, 20001, seed=9, with_bias=True)
 
 
 def _mask(M, V, seed):
@@ -334,9 +335,11 @@ def test_chunk_sizes_and_extras(wide_case, M, chunk_rows, extras):
 # the two accumulation chains (quads [0, Qh) and [Qh, Q), Qh = floor(Q / 2)):
 # one wave running both (1,024 and 2,048-row chunks) and two waves sharing a
 # tile (512 and 64-row chunks) give the same bits for every group count,
-# including an empty first chain (G <= 3) and a partial last quad
+# including an empty first chain (G <= 3) and a partial last quad; from
+# G = 16 on (four quads per chain and G % 4 == 0) 1,024-row chunks with
+# four to six rows share the second chains out as tasks
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 7, 8, 9, 12, 13])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 7, 8, 9, 12, 13, 16, 20, 24])
 @pytest.mark.parametrize("M", [1, 2, 5])
 def test_split_chains_bitwise_across_chunk_sizes(M, G):
     c = Case(M, 128 * G, 3001, seed=G, with_bias=True)
@@ -370,3 +373,17 @@ def test_logits_follow_the_documented_fp32_order(M, G, C):
     c = Case(M, 128 * G, 3001, seed=100 + G, with_bias=True)
     v, i = c.run(12, chunk_rows=C)
     assert_documented_fp32_order(c, v, i, list(range(M)))
+
+
+@pytest.mark.parametrize("V", [3072 + 50, 1024 + 64, 4 * 1024, 2000])
+@pytest.mark.parametrize("M", [1, 4, 6])
+def test_chain_tasks_ragged_last_chunk(M, V):
+    """1,024-row chunks whose last chunk has from one tile up to all 16: with
+    four to six rows the waves without a tile of their own take no task,
+    the others take every second chain of the tiles that exist (one row:
+    the fixed assignment)."""
+    c = Case(M, 2048, V, seed=V, with_bias=True)
+    v0, i0, _ = c.check(40, chunk_rows=1024)
+    v, i = c.run(40, chunk_rows=512)
+    assert torch.equal(i, i0) and torch.equal(v.view(torch.int32), v0.view(torch.int32))
+    assert_documented_fp32_order(c, v0, i0, list(range(M)), n=8)

@@ -204,9 +204,14 @@ def test_lse_output_is_the_sampled_normaliser():
         assert np.allclose(lse.cpu().numpy(), want, rtol=0, atol=1e-5 + 2.0**-22 * np.abs(want).max() * 4)
 
 
-@pytest.mark.parametrize("path", ["binary", "dense"])
-def test_fused_paths_draw_like_the_oracle(path):
-    M, H, V, k = 3, 1024, 32001, 50
+@pytest.mark.parametrize("path,M,H,chunk_rows", [
+    ("binary", 3, 1024, 0),
+    # five rows, 1,024-row chunks, G = 16: the second chains run as tasks
+    ("binary", 5, 2048, 1024),
+    ("dense", 3, 1024, 0),
+])
+def test_fused_paths_draw_like_the_oracle(path, M, H, chunk_rows):
+    V, k = 32001, 50
     T, tk, tp, mp = 0.7, 40, 0.9, 0.0
     if path == "binary":
         W = synthetic.dense_head(V, H, 3)
@@ -227,7 +232,7 @@ def test_fused_paths_draw_like_the_oracle(path):
         kept = torch.empty(M, dtype=torch.int32, device="cuda")
         if path == "binary":
             v, i, t = lt.lm_head_topk_binary(dev(act_q), dev(act_scale), wq, ws, bias=dev(bias), k=k,
-                                             sampling=s, kept=kept)
+                                             sampling=s, kept=kept, chunk_rows=chunk_rows)
         else:
             v, i, t = lt.lm_head_topk_dense(dev(hid), dev(W), k=k, sampling=s, kept=kept)
         torch.cuda.synchronize()
