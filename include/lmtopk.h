@@ -89,9 +89,10 @@ typedef struct {
      the log-sum-exp of all V of its logits, log(sum_v exp(L[m, v])), so
      that values[m, i] - lse[m] are the top-k log-probabilities (Selective
      Log Softmax page, section "Kernel design", online log-sum-exp: per
-     slice a maximum and a sum of exponentials, then combined).  Each wave
-     of a chunk reduces its rows to one (max, sum) pair and the final merge
-     combines them; no weight byte is read twice.  An +inf logit gives +inf;
+     slice a maximum and a sum of exponentials, then combined).  Each chunk
+     reduces its rows to one (max, sum) pair (its waves' pairs combined in
+     LDS) and the final merge combines the chunks' pairs; no weight byte is
+     read twice.  An +inf logit gives +inf;
      a row whose logits are all -inf gives -inf.  16-byte aligned. */
   float* lse;
   /* If not NULL: a device bitmask [M][ceil(V / 32)] of int32 words; bit
@@ -217,8 +218,7 @@ lmtopk_status lmtopk_packed_bytes(int64_t V, int64_t H, int32_t group_size,
    when they fit it, instead of a second launch), then, per row and chunk,
    the chunk's four best candidates and all its candidates (8 bytes each),
    plus one intermediate merge level when a row has more than 16384
-   candidates, plus 8 bytes per row, chunk and wave for the log-sum-exp
-   partials.
+   candidates, plus 8 bytes per row and chunk for the log-sum-exp pairs.
    Errors: NULL, SHAPE, K, OPTIONS. */
 lmtopk_status lmtopk_workspace_bytes(int64_t M, int64_t V, int32_t k,
                                      const lmtopk_options* opt, size_t* bytes);

@@ -114,7 +114,7 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, int s
     g->fused = 1;
     g->n_levels = 0;
   }
-  g->lse_bytes = round_up((size_t)(M * g->n_chunks * g->nw * 8), 256);
+  g->lse_bytes = round_up((size_t)(M * g->n_chunks * 8), 256);
   g->workspace_bytes =
       g->sync_bytes + g->heads_bytes + g->region0_bytes + g->region1_bytes + g->lse_bytes;
   return LMTOPK_OK;

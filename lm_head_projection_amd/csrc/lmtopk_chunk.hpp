@@ -33,7 +33,7 @@ struct FusedMerge {
   int n_chunks;
   int kc;
   int k;
-  const uint2* lse_part;  // [M][n_chunks][waves] (max, sum) pairs, or null
+  const uint2* lse_part;  // [M][n_chunks] log-sum-exp pairs, or null
   float* lse;             // [M] or null
   SampleParams smp;       // the token draw (smp.on == 0: none)
 };
@@ -63,7 +63,7 @@ __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem
   lds_barrier();
   if (uniform(last) == 0u) return;
   const int64_t n_in = (int64_t)f.n_chunks * f.kc;
-  const int n_part = f.n_chunks * (int)(blockDim.x >> 6);
+  const int n_part = f.n_chunks;  // one log-sum-exp pair per chunk and row
   for (int m = 0; m < f.M; ++m) {
     // the row's log-sum-exp partials and draw parameters are requested
     // before the merge, which waits for its own loads meanwhile
@@ -78,7 +78,7 @@ __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem
     lds_barrier();  // fs.out_* are complete; fs is reused by the next row
     float lse = 0.f;
     if (kExtras && f.lse_part != nullptr)
-      lse = merge_lse(f.lse_part + (size_t)m * n_part, n_part, f.lse ? f.lse + m : nullptr, sm, have,
+      lse = merge_lse(f.lse_part + (size_t)m * n_part, n_part, f.lse ? f.lse + m : nullptr, fs, have,
                       pre, kSample && f.smp.on);
     if (kSample && f.smp.on) {
       sample_row(fs.out_bits, fs.out_idx, f.k, lse, rs, m, f.smp);
@@ -100,7 +100,7 @@ struct ChunkOut {
   int k;
   int M;
   int fused;          // the launch's last workgroup merges (fused_merge_tail)
-  uint2* lse_part;    // log-sum-exp partials [M][n_chunks][waves], or null
+  uint2* lse_part;    // log-sum-exp pairs [M][n_chunks], or null
   float* lse;         // [M] or null
   const int32_t* allowed;  // bitmask [M][allowed_words] (bit 1 = allowed), or null
   int allowed_words;       // ceil(V / 32)
@@ -177,8 +177,10 @@ __device__ __forceinline__ void chunk_select_write(const float (&val_in)[RPL], c
   }
   const size_t row_chunk = (size_t)m * o.n_chunks + blockIdx.x;
   if (kExtras && o.lse_part != nullptr) {
-    // this wave's (max, sum of exp(logit - max)) over its valid rows
+    // this wave's log-sum-exp pair (max, sum of exp(z - max)) over its valid
+    // rows, z = zs * logit
     const int wave = wave_id();
+    const int lane = lane_id();
     float z[RPL];
 #pragma unroll
     for (int r = 0; r < RPL; ++r) z[r] = val[r] * zs;
@@ -194,9 +196,26 @@ __device__ __forceinline__ void chunk_select_write(const float (&val_in)[RPL], c
         if ((valid >> r) & 1u) sum += expf(z[r] - mx);
     }
     sum = wave_sum_f32(sum);
-    if (lane_id() == 0)
-      st_cand(&o.lse_part[row_chunk * (blockDim.x >> 6) + wave],
-              make_uint2(__float_as_uint(mx), __float_as_uint(sum)));
+    // The chunk's pair: every wave posts its pair; the wave that posts last
+    // combines them (lane w holds wave w's pair) and stores it.
+    if (lane == 0) st.lse_w[m][wave] = make_uint2(__float_as_uint(mx), __float_as_uint(sum));
+    // the pair is written before the count (LDS operations of a wave
+    // complete in order; the fence keeps the compiler from reordering)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    uint32_t done = 0u;
+    if (lane == 0) done = atomicAdd(&st.lse_done[m], 1u);
+    done = readlane_u32(done, 0);
+    if (done == (blockDim.x >> 6) - 1u) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      float cm = -INFINITY, cs = 0.f;
+      if (lane < (int)(blockDim.x >> 6)) {
+        const uint2 p = st.lse_w[m][lane];
+        cm = __uint_as_float(p.x);
+        cs = __uint_as_float(p.y);
+      }
+      lse_combine_wave(cm, cs);
+      if (lane == 0) st_cand(&o.lse_part[row_chunk], make_uint2(__float_as_uint(cm), __float_as_uint(cs)));
+    }
   }
   uint2* out = o.cand + row_chunk * o.kc;
   uint2* heads = o.heads + row_chunk * kHeads;

@@ -34,6 +34,7 @@ namespace lmtopk {
 
 constexpr int kWave = 64;
 constexpr int kMaxWaves = 16;
+constexpr int kMaxRows = 8;  // activation rows per call
 constexpr int kMaxK = 2048;
 
 // Order-preserving map fp32 -> uint32 (larger float => larger key).  -0.0 is
@@ -177,7 +178,6 @@ struct alignas(16) SelectSmem {
   uint32_t wcnt[kMaxWaves];
   uint32_t cgt[kMaxWaves];
   uint32_t ceq[kMaxWaves];
-  float lse_out;  // merge_lse's result, for every thread of the workgroup
 };
 
 // Outcome of the search: keys k with (k & mask) > prefix are all selected;
@@ -378,6 +378,10 @@ struct alignas(16) HeadStage {
   uint32_t tops_done;  // provider waves that have published their tops
   uint32_t thr_ready;  // thr is valid
   uint32_t thr;        // T
+  // the chunk's log-sum-exp pairs: one per wave and row, and per row the
+  // waves that have posted theirs (zero from head_stage_init on)
+  uint2 lse_w[kMaxRows][kMaxWaves];
+  uint32_t lse_done[kMaxRows];
 };
 
 // Puts st in the state select_top_small and block_heads expect on entry;
@@ -389,6 +393,7 @@ __device__ __forceinline__ void head_stage_init(HeadStage& st) {
     st.tops_done = 0u;
     st.thr_ready = 0u;
   }
+  if (threadIdx.x < kMaxRows) st.lse_done[threadIdx.x] = 0u;
 }
 
 // Counting over n entries in LDS, for each entry i < n:
@@ -687,6 +692,7 @@ struct alignas(16) FinalSmem {
   // the row's result in output order, kept for the token draw
   uint32_t out_bits[kMaxK];
   int32_t out_idx[kMaxK];
+  uint2 lse_w[kMaxWaves];  // merge_lse: each wave's log-sum-exp pair
 };
 
 // Entries [0, n) of fs are filled, [n, 4 * ceil(n / 4)) hold padding that is
@@ -905,19 +911,37 @@ __device__ __forceinline__ void merge_final(const uint2* in, int64_t n_in, const
   rank_and_write(fs, n, k, values, indices);
 }
 
-// Log-sum-exp of one row (Selective Log Softmax page, section "Kernel
-// design": per-slice maxima and sums of exponentials, combined), returned to
-// every thread when `want` (else 0) and written to *out (unless out is
-// null).  part[0, n)
-// holds one (max, sum) pair per wave and chunk of the row, sum = the sum of
-// exp(logit - max) over that wave's rows (max -inf: no finite rows, sum 0;
-// max +inf: an +inf logit).  With M the largest max, the row's log-sum-exp
-// is M + log(sum of pair.sum * exp(pair.max - M)); +inf if M is +inf, -inf
-// if M is -inf.  Called by the whole workgroup; sm's wave slots are reused,
-// and the reductions run in a fixed order.
-// A thread's pairs i = thread + j * blockDim (j < kLsePairs) may be loaded
-// by the caller ahead of time (load_lse_pairs), so that their round trip
-// overlaps other work; rows with more pairs are read in the loop.
+// Log-sum-exp pairs (Selective Log Softmax page, section "Kernel design":
+// per-slice maxima and sums of exponentials, combined).  A pair (m, s)
+// stands for m + log(s): m the largest logit of a slice and s the sum of
+// exp(logit - m) over it; (-inf, 0) is an empty slice (or one of -inf
+// logits only) and (+inf, 1) a slice with an +inf logit.  Pairs combine as
+// (M, sum of s_i exp(m_i - M)), M the largest m_i: M is +inf or -inf for
+// the whole set when it is for the result.
+//
+// Combines the pairs held by the lanes of one wave (absent lanes hold
+// (-inf, 0)) into the pair every lane returns: the wave's maximum, then
+// the wave's sum of the rescaled s (fixed reduction orders).
+__device__ __forceinline__ void lse_combine_wave(float& m, float& s) {
+  const float M = wave_max_f32(m);
+  float t = 0.f;
+  if (M == INFINITY) t = m == INFINITY ? 1.f : 0.f;  // one +inf slice counts once
+  else if (M != -INFINITY && m != -INFINITY) t = s * expf(m - M);
+  s = wave_sum_f32(t);
+  if (M == INFINITY) s = 1.f;
+  m = M;
+}
+
+// Log-sum-exp of one row from part[0, n), one pair per chunk of the row,
+// returned to every thread when `want` (else 0) and written to *out (unless
+// out is null): the maximum M over the pairs (per thread, per wave, then
+// every wave over the waves' maxima in fs.lse_w), then the sum of
+// s * exp(m - M) the same way; fixed reduction orders, two barriers.
+// Called by the whole workgroup; fs.lse_w is not written again before the
+// caller's next barrier.
+// A thread's pairs (j < kLsePairs) may be loaded by the caller ahead of time
+// (load_lse_pairs), so that their round trip overlaps other work; rows with
+// more pairs are read in the loop.
 constexpr int kLsePairs = 4;
 __device__ __forceinline__ bool load_lse_pairs(const uint2* part, int n, uint2 (&p)[kLsePairs]) {
   const bool fits = n <= kLsePairs * (int)blockDim.x;
@@ -929,13 +953,14 @@ __device__ __forceinline__ bool load_lse_pairs(const uint2* part, int n, uint2 (
   return fits;
 }
 
-__device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out, SelectSmem& sm,
+__device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out, FinalSmem& fs,
                                           bool have, const uint2 (&pre)[kLsePairs],
                                           bool want = true) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
   const int nw = blockDim.x >> 6;
+  // 1. the row's maximum M
   float mx = -INFINITY;
   if (have) {
 #pragma unroll
@@ -944,16 +969,16 @@ __device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out,
     for (int i = tid; i < n; i += (int)blockDim.x) mx = fmaxf(mx, __uint_as_float(ld_cand(&part[i]).x));
   }
   mx = wave_max_f32(mx);
-  if (lane == 0) sm.wmax[wave] = __float_as_uint(mx);
+  if (lane == 0) fs.lse_w[wave].x = __float_as_uint(mx);
   lds_barrier();
-  float M = -INFINITY;
-  for (int w = 0; w < nw; ++w) M = fmaxf(M, __uint_as_float(sm.wmax[w]));
+  const float M = wave_max_f32(lane < nw ? __uint_as_float(fs.lse_w[lane].x) : -INFINITY);
+  // 2. the sum of s * exp(m - M) (every wave computes the total)
   float sum = 0.f;
-  auto add = [&](const uint2& p) {
-    const float pm = __uint_as_float(p.x);
-    if (pm != -INFINITY) sum += __uint_as_float(p.y) * expf(pm - M);
-  };
   if (M != INFINITY && M != -INFINITY) {
+    auto add = [&](const uint2& p) {
+      const float pm = __uint_as_float(p.x);
+      if (pm != -INFINITY) sum += __uint_as_float(p.y) * expf(pm - M);
+    };
     if (have) {
 #pragma unroll
       for (int j = 0; j < kLsePairs; ++j) add(pre[j]);
@@ -962,22 +987,12 @@ __device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out,
     }
   }
   sum = wave_sum_f32(sum);
-  if (lane == 0) sm.wmin[wave] = __float_as_uint(sum);
+  if (lane == 0) fs.lse_w[wave].y = __float_as_uint(sum);
   lds_barrier();
-  if (tid == 0) {
-    float S = 0.f;
-    for (int w = 0; w < nw; ++w) S += __uint_as_float(sm.wmin[w]);
-    const float r = M == INFINITY ? INFINITY : M == -INFINITY ? -INFINITY : M + logf(S);
-    if (out != nullptr) *out = r;
-    sm.lse_out = r;
-  }
-  lds_barrier();
-  float r = 0.f;
-  if (want) {  // every thread reads the result (sm.lse_out), then sm may be reused
-    r = sm.lse_out;
-    lds_barrier();
-  }
-  return r;
+  const float S = wave_sum_f32(lane < nw ? __uint_as_float(fs.lse_w[lane].y) : 0.f);
+  const float r = M == INFINITY ? INFINITY : M == -INFINITY ? -INFINITY : M + logf(S);
+  if (tid == 0 && out != nullptr) *out = r;
+  return want ? r : 0.f;
 }
 
 }  // namespace lmtopk

@@ -61,7 +61,7 @@ struct Geometry {
   size_t heads_bytes;    // best candidates of each chunk [M][n_chunks][4] x 8 B
   size_t region0_bytes;  // chunk candidates [M][n_chunks * kc] x 8 B
   size_t region1_bytes;  // first intermediate merge output, or 0
-  size_t lse_bytes;      // log-sum-exp partials [M][n_chunks][nw] x (max, sum)
+  size_t lse_bytes;      // log-sum-exp pairs [M][n_chunks] x (max, sum)
   size_t workspace_bytes;
   float* lse;            // this call's log-sum-exp output [M], or null (not part of the plan)
   const int32_t* allowed;  // this call's bitmask [M][ceil(V/32)], or null (not part of the plan)

@@ -143,7 +143,7 @@ struct MergeArgs {
   uint2* out;       // intermediate: [M][n_seg][k]
   float* values;    // final: [M][k]
   int64_t* indices; // final: [M][k]
-  const uint2* lse_part;  // final: log-sum-exp partials [M][n_part], or null
+  const uint2* lse_part;  // final: log-sum-exp pairs [M][n_part] (one per chunk), or null
   int n_part;
   float* lse;             // final: [M] or null
   SampleParams smp;       // final: the token draw (smp.on == 0: none)
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
     lds_barrier();  // ssm is reused; fs.out_* are complete
     float lse = 0.f;
     if (a.lse_part != nullptr)
-      lse = merge_lse(a.lse_part + (size_t)m * a.n_part, a.n_part, a.lse ? a.lse + m : nullptr, ssm, have, pre);
+      lse = merge_lse(a.lse_part + (size_t)m * a.n_part, a.n_part, a.lse ? a.lse + m : nullptr, fs, have, pre);
     if (a.smp.on) sample_row(fs.out_bits, fs.out_idx, a.k, lse, rs, m, a.smp);
     return;
   }
@@ -311,7 +311,7 @@ int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* in
     a.values = values;
     a.indices = indices;
     a.lse = g.lse;
-    a.n_part = g.n_chunks * g.nw;
+    a.n_part = g.n_chunks;
     a.lse_part = (g.lse || g.smp.need_norm)
                      ? reinterpret_cast<const uint2*>(ws + g.region0_bytes + g.region1_bytes)
                      : nullptr;
