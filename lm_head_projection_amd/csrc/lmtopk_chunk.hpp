@@ -68,7 +68,7 @@ __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem
     // the row's log-sum-exp partials and draw parameters are requested
     // before the merge, which waits for its own loads meanwhile
     uint2 pre[kLsePairs];
-    bool have = false;
+    int have = 0;
     if (kExtras && f.lse_part != nullptr) have = load_lse_pairs(f.lse_part + (size_t)m * n_part, n_part, pre);
     RowSample rs;
     if (kSample && f.smp.on) rs = load_row_sample(f.smp, m);
@@ -76,12 +76,17 @@ __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem
                     f.n_chunks, f.kc, (uint32_t)f.k, f.values + (size_t)m * f.k,
                     f.indices + (size_t)m * f.k, (int)blockDim.x, sm, fs);
     lds_barrier();  // fs.out_* are complete; fs is reused by the next row
+    // the log-sum-exp (wave 0, or the workgroup for many chunks) and the
+    // draw's noise (another wave) at the same time, then the draw
     float lse = 0.f;
     if (kExtras && f.lse_part != nullptr)
       lse = merge_lse(f.lse_part + (size_t)m * n_part, n_part, f.lse ? f.lse + m : nullptr, fs, have,
                       pre, kSample && f.smp.on);
     if (kSample && f.smp.on) {
-      sample_row(fs.out_bits, fs.out_idx, f.k, lse, rs, m, f.smp);
+      float* noise = reinterpret_cast<float*>(fs.key);  // free after the merge
+      draw_noise(fs.out_idx, f.k, rs, m, f.smp, noise);
+      lds_barrier();
+      sample_row(fs.out_bits, fs.out_idx, noise, f.k, lse, rs, m, f.smp);
       lds_barrier();  // fs is reused by the next row
     }
   }

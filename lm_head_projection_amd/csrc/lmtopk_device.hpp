@@ -933,33 +933,40 @@ __device__ __forceinline__ void lse_combine_wave(float& m, float& s) {
 }
 
 // Log-sum-exp of one row from part[0, n), one pair per chunk of the row,
-// returned to every thread when `want` (else 0) and written to *out (unless
-// out is null): the maximum M over the pairs (per thread, per wave, then
-// every wave over the waves' maxima in fs.lse_w), then the sum of
-// s * exp(m - M) the same way; fixed reduction orders, two barriers.
+// written to *out (unless out is null) and returned to the threads named
+// below when `want` (else 0).  The maximum M over the pairs, then the sum of
+// s * exp(m - M), each in a fixed order.
+//   mode 1 (n <= 64 * kLsePairs): wave 0 alone, from the pairs it preloaded
+//     (lane l: pairs l + 64 j); no barrier; the result goes to wave 0.
+//   mode 2 (n <= kLsePairs * threads): every thread from its preloaded pairs
+//     (i = thread + j * threads), each wave, then every wave over the
+//     waves' values in fs.lse_w; two barriers; the result goes to all.
+//   mode 0: as mode 2, with the pairs read here.
 // Called by the whole workgroup; fs.lse_w is not written again before the
-// caller's next barrier.
-// A thread's pairs (j < kLsePairs) may be loaded by the caller ahead of time
-// (load_lse_pairs), so that their round trip overlaps other work; rows with
-// more pairs are read in the loop.
+// caller's next barrier.  Preloading (load_lse_pairs) lets the pairs' round
+// trip overlap the merge.
 constexpr int kLsePairs = 4;
-__device__ __forceinline__ bool load_lse_pairs(const uint2* part, int n, uint2 (&p)[kLsePairs]) {
-  const bool fits = n <= kLsePairs * (int)blockDim.x;
+__device__ __forceinline__ int load_lse_pairs(const uint2* part, int n, uint2 (&p)[kLsePairs]) {
+  const int mode = n <= 64 * kLsePairs ? 1 : n <= kLsePairs * (int)blockDim.x ? 2 : 0;
+  const bool mine = mode == 2 || (mode == 1 && wave_id() == 0);
+  const int step = mode == 1 ? 64 : (int)blockDim.x;
 #pragma unroll
   for (int j = 0; j < kLsePairs; ++j) {
-    const int i = (int)threadIdx.x + j * (int)blockDim.x;
-    p[j] = fits && i < n ? ld_cand(&part[i]) : make_uint2(__float_as_uint(-INFINITY), 0u);
+    const int i = (int)threadIdx.x + j * step;
+    p[j] = mine && i < n ? ld_cand(&part[i]) : make_uint2(__float_as_uint(-INFINITY), 0u);
   }
-  return fits;
+  return mode;
 }
 
 __device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out, FinalSmem& fs,
-                                          bool have, const uint2 (&pre)[kLsePairs],
+                                          int mode, const uint2 (&pre)[kLsePairs],
                                           bool want = true) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
   const int nw = blockDim.x >> 6;
+  const bool have = mode != 0;
+  if (mode == 1 && wave != 0) return 0.f;
   // 1. the row's maximum M
   float mx = -INFINITY;
   if (have) {
@@ -969,10 +976,13 @@ __device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out,
     for (int i = tid; i < n; i += (int)blockDim.x) mx = fmaxf(mx, __uint_as_float(ld_cand(&part[i]).x));
   }
   mx = wave_max_f32(mx);
-  if (lane == 0) fs.lse_w[wave].x = __float_as_uint(mx);
-  lds_barrier();
-  const float M = wave_max_f32(lane < nw ? __uint_as_float(fs.lse_w[lane].x) : -INFINITY);
-  // 2. the sum of s * exp(m - M) (every wave computes the total)
+  float M = mx;
+  if (mode != 1) {
+    if (lane == 0) fs.lse_w[wave].x = __float_as_uint(mx);
+    lds_barrier();
+    M = wave_max_f32(lane < nw ? __uint_as_float(fs.lse_w[lane].x) : -INFINITY);
+  }
+  // 2. the sum of s * exp(m - M)
   float sum = 0.f;
   if (M != INFINITY && M != -INFINITY) {
     auto add = [&](const uint2& p) {
@@ -987,9 +997,12 @@ __device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out,
     }
   }
   sum = wave_sum_f32(sum);
-  if (lane == 0) fs.lse_w[wave].y = __float_as_uint(sum);
-  lds_barrier();
-  const float S = wave_sum_f32(lane < nw ? __uint_as_float(fs.lse_w[lane].y) : 0.f);
+  float S = sum;
+  if (mode != 1) {
+    if (lane == 0) fs.lse_w[wave].y = __float_as_uint(sum);
+    lds_barrier();
+    S = wave_sum_f32(lane < nw ? __uint_as_float(fs.lse_w[lane].y) : 0.f);
+  }
   const float r = M == INFINITY ? INFINITY : M == -INFINITY ? -INFINITY : M + logf(S);
   if (tid == 0 && out != nullptr) *out = r;
   return want ? r : 0.f;

@@ -87,12 +87,37 @@ __device__ __forceinline__ float wave_scan_inclusive_f32(float v) {
   return v;
 }
 
+// The positions a row's draw can keep: the top-k limit.
+__device__ __forceinline__ int draw_limit(const RowSample& rs, int k) {
+  return (rs.top_k <= 0 || rs.top_k >= k) ? k : rs.top_k;
+}
+
+// Gumbel noise g_i = -log(-log(u_i)) of positions i < limit of row m's
+// survivors (idx [0, k) in LDS, output order), u_i from the Philox stream
+// of (vocabulary index, row, offset) under (seed), into g[i].  One wave
+// does it (wave 1 when there is one, so that it overlaps wave 0's
+// log-sum-exp); the caller orders g with a barrier before sample_row.
+__device__ __forceinline__ void draw_noise(const int32_t* idx, int k, const RowSample& rs, int m,
+                                           const SampleParams& s, float* g) {
+  const int noise_wave = (blockDim.x >> 6) > 1 ? 1 : 0;
+  if (wave_id() != noise_wave) return;
+  const int limit = draw_limit(rs, k);
+  const uint64_t off = rs.offset;
+  for (int i = lane_id(); i < limit; i += 64) {
+    const uint32_t x = philox_word0((uint32_t)idx[i], (uint32_t)m, (uint32_t)off,
+                                    (uint32_t)(off >> 32), (uint32_t)s.seed,
+                                    (uint32_t)(s.seed >> 32));
+    g[i] = -logf(-logf(uniform_of(x)));
+  }
+}
+
 // Draws row m's token from its k survivors (bits / idx [0, k) in LDS, output
-// order) and writes tokens[m] (and kept[m]).  lse: the normaliser of the
-// scaled logits (read only when top-p is on).  Called by every thread of the
-// workgroup; wave 0 does the work; no barrier inside.
-__device__ __forceinline__ void sample_row(const uint32_t* bits, const int32_t* idx, int k,
-                                           float lse, const RowSample& rs, int m,
+// order; g [0, limit) their Gumbel noise from draw_noise) and writes
+// tokens[m] (and kept[m]).  lse: the normaliser of the scaled logits (read
+// only when top-p is on).  Called by every thread of the workgroup; wave 0
+// does the work; no barrier inside.
+__device__ __forceinline__ void sample_row(const uint32_t* bits, const int32_t* idx, const float* g,
+                                           int k, float lse, const RowSample& rs, int m,
                                            const SampleParams& s) {
   if (wave_id() != 0) return;
   const int lane = lane_id();
@@ -102,7 +127,7 @@ __device__ __forceinline__ void sample_row(const uint32_t* bits, const int32_t* 
   if (!greedy) {
     const float zs = 1.f / rs.temperature;
     const float z0 = L0 * zs;
-    const int limit = (rs.top_k <= 0 || rs.top_k >= k) ? k : rs.top_k;
+    const int limit = draw_limit(rs, k);
     const bool use_p = rs.top_p < 1.f;
     const bool use_m = rs.min_p > 0.f;
     const int J = (k + 63) >> 6;
@@ -133,17 +158,12 @@ __device__ __forceinline__ void sample_row(const uint32_t* bits, const int32_t* 
     n_keep = wave_min_u32(stop);
     // Gumbel-max over the kept prefix; a lane's positions ascend, so its
     // first maximum is its lowest position
-    const uint64_t off = rs.offset;
     float best = -INFINITY;
     uint32_t best_i = 0xFFFFFFFFu;
     for (int j = 0; j < J; ++j) {
       const int i = i0 + j;
       if (i >= (int)n_keep) break;
-      const uint32_t x = philox_word0((uint32_t)idx[i], (uint32_t)m, (uint32_t)off,
-                                      (uint32_t)(off >> 32), (uint32_t)s.seed,
-                                      (uint32_t)(s.seed >> 32));
-      const float g = -logf(-logf(uniform_of(x)));
-      const float v = __uint_as_float(bits[i]) * zs + g;
+      const float v = __uint_as_float(bits[i]) * zs + g[i];
       if (v > best) {
         best = v;
         best_i = (uint32_t)i;

@@ -163,7 +163,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
   if (a.n_seg == 1) {
     __shared__ FinalSmem fs;
     uint2 pre[kLsePairs];
-    bool have = false;
+    int have = 0;
     if (a.lse_part != nullptr) have = load_lse_pairs(a.lse_part + (size_t)m * a.n_part, a.n_part, pre);
     RowSample rs;
     if (a.smp.on) rs = load_row_sample(a.smp, m);
@@ -174,7 +174,12 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
     float lse = 0.f;
     if (a.lse_part != nullptr)
       lse = merge_lse(a.lse_part + (size_t)m * a.n_part, a.n_part, a.lse ? a.lse + m : nullptr, fs, have, pre);
-    if (a.smp.on) sample_row(fs.out_bits, fs.out_idx, a.k, lse, rs, m, a.smp);
+    if (a.smp.on) {
+      float* noise = reinterpret_cast<float*>(fs.key);  // free after the merge
+      draw_noise(fs.out_idx, a.k, rs, m, a.smp, noise);
+      lds_barrier();
+      sample_row(fs.out_bits, fs.out_idx, noise, a.k, lse, rs, m, a.smp);
+    }
     return;
   }
   const int wave = wave_id();
