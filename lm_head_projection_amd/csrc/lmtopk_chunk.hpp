@@ -110,6 +110,9 @@ struct ChunkOut {
   const int32_t* allowed;  // bitmask [M][allowed_words] (bit 1 = allowed), or null
   int allowed_words;       // ceil(V / 32)
   SampleParams smp;        // the token draw (smp.on == 0: none)
+  // select_top_small's providers (small_select_plan): P and h for a full
+  // chunk and for the last one
+  int sel_p[2], sel_h[2];
 };
 
 // The fused merge's view of a chunk launch's outputs.
@@ -224,8 +227,10 @@ __device__ __forceinline__ void chunk_select_write(const float (&val_in)[RPL], c
   }
   uint2* out = o.cand + row_chunk * o.kc;
   uint2* heads = o.heads + row_chunk * kHeads;
-  if (o.k <= kWaveTops * (int)(blockDim.x >> 6)) {
-    const uint32_t n = select_top_small<RPL>(key, valid, vb, idx, (uint32_t)o.k, st,
+  const int plan = blockIdx.x == (unsigned)o.n_chunks - 1u ? 1 : 0;  // the last chunk may be partial
+  if (o.k <= kWaveTops * (int)(blockDim.x >> 6) && o.sel_p[plan] >= 0) {
+    const uint32_t n = select_top_small<RPL>(key, valid, vb, idx, (uint32_t)o.k, o.sel_p[plan],
+                                             o.sel_h[plan], st,
                                              [&](uint32_t pos, uint32_t bits, int32_t ix) {
                                                const uint2 e = make_uint2(bits, (uint32_t)ix);
                                                st_cand(&out[pos], e);
@@ -314,6 +319,14 @@ inline ChunkOut chunk_out(const Geometry& g, void* workspace, float* values, int
   o.lse = g.lse;
   o.allowed = g.allowed;
   o.allowed_words = (int)((g.V + 31) / 32);
+  {
+    const int nw = g.nw;
+    const int cap = g.chunk_rows / nw;  // rows per wave, in row order
+    const int kk = g.k < g.chunk_rows ? g.k : g.chunk_rows;
+    o.sel_p[0] = small_select_plan(kk, nw, cap, g.chunk_rows, &o.sel_h[0]);
+    o.sel_p[1] = small_select_plan(kk, nw, cap, g.V - (int64_t)(g.n_chunks - 1) * g.chunk_rows,
+                                   &o.sel_h[1]);
+  }
   o.lse_part = (g.lse || g.smp.need_norm)
                    ? reinterpret_cast<uint2*>(ws + g.sync_bytes + g.heads_bytes + g.region0_bytes +
                                               g.region1_bytes)

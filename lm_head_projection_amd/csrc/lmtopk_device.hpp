@@ -362,6 +362,33 @@ constexpr int kWaveTops = 4;
 // ... and gives up (the radix select runs) above this many survivors.
 constexpr uint32_t kSmallSurvivorsMax = 256;
 
+// Providers of select_top_small for a chunk of n_valid valid rows (its
+// first rows), wave w holding rows [w cap, (w + 1) cap): the first P waves,
+// all of whose rows are valid (3/4 of the waves, fewer in a partial last
+// chunk), each take h = ceil(k / P) tops, with P * h <= 64 and h <= cap (P
+// shrinks until both hold).  Returns P (and h); 0 when no such P exists and
+// at most kSmallSurvivorsMax rows are valid (every valid row is staged), -1
+// otherwise (the radix select runs).  Host and device.
+__host__ __device__ inline int small_select_plan(int k, int nw, int cap, int64_t n_valid, int* h_out) {
+  const int full = (int)(n_valid / cap);
+  int P = (3 * nw) / 4;
+  P = P < 1 ? 1 : P;
+  P = P < full ? P : full;
+  int h = P > 0 ? (k + P - 1) / P : 0;
+  if (P * h > kMaxWaves * kWaveTops) {
+    P = nw < full ? nw : full;
+    h = (k + P - 1) / P;
+  }
+  while (P > 1 && (P * h > kMaxWaves * kWaveTops || h > cap)) {
+    --P;
+    h = (k + P - 1) / P;
+  }
+  *h_out = h;
+  if (P >= 1 && P * h <= kMaxWaves * kWaveTops && h <= cap) return P;
+  *h_out = 0;
+  return n_valid <= (int64_t)kSmallSurvivorsMax ? 0 : -1;
+}
+
 // LDS of the chunk selection's second stage: staged entries, their ranks and
 // the small-k path's per-wave tops.
 struct alignas(16) HeadStage {
@@ -533,10 +560,11 @@ using lds_t = __attribute__((address_space(3))) T;
 constexpr int kThresholdSpinMax = 1 << 22;
 
 // Exact top-k of one chunk row for small k (k <= kWaveTops * waves), without
-// radix passes.  The first P = 3/4 of the waves (the "providers") each take
-// their h = ceil(k / P) largest keys (P * h <= 64; else P = all waves); the
-// provider that completes this set finds T, the k-th largest of the P * h
-// tops, alone and publishes it.  T is at most the chunk's k-th largest key
+// radix passes.  The first P waves (the "providers", all of whose rows are
+// valid; `small_select_plan`) each take their h largest keys; the provider
+// that completes this set finds T, the k-th largest of the P h tops, alone
+// and publishes it.  P = 0: every valid row is staged (a last chunk of at
+// most kSmallSurvivorsMax rows).  T is at most the chunk's k-th largest key
 // (the tops are real entries of the chunk), so every winner has key >= T.
 // Every wave stages its rows with key >= T as soon as T is published: the
 // waves a CU serves first have finished streaming long before the last
@@ -552,22 +580,16 @@ constexpr int kThresholdSpinMax = 1 << 22;
 template <int R, typename Out>
 __device__ uint32_t select_top_small(const uint32_t (&key)[R], uint32_t valid,
                                      const uint32_t (&vbits)[R], const int32_t (&index)[R],
-                                     uint32_t k, HeadStage& st, Out&& out) {
+                                     uint32_t k, int P, int h, HeadStage& st, Out&& out) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
-  const int nw = blockDim.x >> 6;
-  int P = max(1, (3 * nw) / 4);
-  int h = ((int)k + P - 1) / P;
-  if (P * h > kMaxWaves * kWaveTops) {
-    P = nw;
-    h = ((int)k + nw - 1) / nw;  // <= kWaveTops
-  }
   P = uniform(P);
   h = uniform(h);
+  const bool stage_all = P == 0;
 
   // 1. providers: this wave's h largest keys (repeats count), 0 where absent
-  if (wave < P) {
+  if (!stage_all && wave < P) {
     uint32_t left = valid, top = 0u;
     for (int j = 0; j < h; ++j) {
       uint32_t best = 0u;
@@ -614,7 +636,7 @@ __device__ uint32_t select_top_small(const uint32_t (&key)[R], uint32_t valid,
   //    superset of the winners), then stage the rows with key >= T (one
   //    atomic per wave reserves its slots)
   uint32_t ready = 0u;
-  for (int spin = 0; spin < kThresholdSpinMax; ++spin) {
+  for (int spin = 0; !stage_all && spin < kThresholdSpinMax; ++spin) {
     ready = uniform(*(volatile lds_t<uint32_t>*)&st.thr_ready);
     if (ready) break;
     __builtin_amdgcn_s_sleep(2);
