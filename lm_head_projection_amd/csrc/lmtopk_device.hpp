@@ -73,6 +73,7 @@ template <int kCtrl, int kRowMask = 0xF, bool kBoundZero = false>
 __device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, kCtrl, kRowMask, 0xF, kBoundZero);
 }
+constexpr int kQuadBcast0 = 0x00;    // quad_perm [0,0,0,0]
 constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;
@@ -779,6 +780,45 @@ __device__ __forceinline__ void place_survivor(FinalSmem& fs, bool take, uint32_
   }
 }
 
+// merge_final's full path with R slots per thread (n_in <= R * nthreads):
+// radix select over every candidate (slot order = index order), ordered
+// compaction, rank and write.
+template <int R>
+__device__ __forceinline__ void merge_full(const uint2* in, int64_t n_in, uint32_t k, float* values,
+                                           int64_t* indices, int nthreads, SelectSmem& sm,
+                                           FinalSmem& fs) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  uint32_t key[R], vb[R];
+  int32_t idx[R];
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t pos = (int64_t)(wave * R + r) * 64 + lane;
+    // unconditional (clamped) loads: all R are in flight before the first
+    // wait; slots past n_in are marked invalid below
+    const uint2 x = ld_cand(&in[pos < n_in ? pos : n_in - 1]);
+    vb[r] = x.x;
+    idx[r] = (int32_t)x.y;
+    key[r] = float_key(__uint_as_float(x.x));
+    valid |= (pos < n_in && idx[r] >= 0 ? 1u : 0u) << r;
+  }
+  const SelectRange s = block_select<R>(key, valid, k, sm);
+  const uint32_t n = block_compact<R>(key, valid, s, vb, idx, sm,
+                                       [&](uint32_t pos, uint32_t bits, int32_t ix) {
+                                         fs.key[pos] = float_key(__uint_as_float(bits));
+                                         fs.bits[pos] = bits;
+                                         fs.idx[pos] = ix;
+                                       });
+  for (uint32_t i = n + tid; i < ((n + 3u) & ~3u); i += nthreads) {
+    fs.key[i] = 0u;
+    fs.idx[i] = 0x7FFFFFFF;
+  }
+  lds_barrier();
+  rank_and_write(fs, n, k, values, indices);
+}
+
 // Final merge of one row.  `in` holds the n_in candidates of the n_max chunks
 // (kc per chunk, fp32 value bits and int32 index, index -1 = padding) in
 // ascending index order; RM slots per thread cover them (n_in <=
@@ -809,13 +849,15 @@ __device__ __forceinline__ void merge_final(const uint2* in, int64_t n_in, const
   for (int i = tid; i < kMaxK + 4; i += nthreads) fs.rank[i] = 0u;
 
   if (heads != nullptr && n_max >= (int)k && n_max <= 256 && n_heads <= nthreads) {
-    // Every thread loads one head and the last head of that head's chunk,
-    // unconditionally (indices clamped into the arrays), so all loads are in
-    // flight at once; thread 4c holds chunk c's maximum.
+    // Every thread below n_heads loads one head and, for the first head of a
+    // chunk, that chunk's last head, so all loads are in flight at once;
+    // thread 4c holds chunk c's maximum.
     const int e = min(tid, n_heads - 1);
     const int c = e / kHeads;
-    const uint2 he = ld_cand(&heads[e]);
-    const uint2 hl = ld_cand(&heads[(size_t)c * kHeads + (kHeads - 1)]);
+    const uint2 absent = make_uint2(0u, 0xFFFFFFFFu);
+    const uint2 he = tid < n_heads ? ld_cand(&heads[e]) : absent;
+    const uint2 hl = tid < n_heads && e == c * kHeads ? ld_cand(&heads[(size_t)c * kHeads + (kHeads - 1)])
+                                                        : absent;
     for (int i = tid; i < (int)kSurvivorsMax + 4; i += nthreads) {
       fs.key[i] = 0u;  // padding: below every real key
       fs.idx[i] = 0x7FFFFFFF;
@@ -866,7 +908,12 @@ __device__ __forceinline__ void merge_final(const uint2* in, int64_t n_in, const
     }
     const bool mine = tid < n_heads && (int32_t)he.y >= 0;
     // a chunk with more candidates than heads may hold survivors beyond them
-    const bool over = kc > kHeads && (int32_t)hl.y >= 0 && float_key(__uint_as_float(hl.x)) >= t;
+    // (decided by the chunk's first head thread, which holds the last head,
+    // and passed to the other three threads of the chunk: one quad of lanes)
+    const uint32_t over0 =
+        kc > kHeads && (int32_t)hl.y >= 0 && float_key(__uint_as_float(hl.x)) >= t ? 1u : 0u;
+    static_assert(kHeads == 4, "one chunk's heads are one quad of lanes");
+    const bool over = dpp<kQuadBcast0>(0u, over0) != 0u;
     place_survivor(fs, mine && !over && key >= t, key, he.x, (int32_t)he.y);
     if (tid < n_heads && over && e == c * kHeads) fs.over[atomicAdd(&fs.n_over, 1u)] = c;
     lds_barrier();
@@ -905,32 +952,17 @@ __device__ __forceinline__ void merge_final(const uint2* in, int64_t n_in, const
   }
 
   // Full path: radix select over every candidate (slot order = index order),
-  // ordered compaction, rank.
-  uint32_t key[RM], vb[RM];
-  int32_t idx[RM];
-  uint32_t valid = 0u;
-#pragma unroll
-  for (int r = 0; r < RM; ++r) {
-    const int64_t pos = (int64_t)(wave * RM + r) * 64 + lane;
-    const uint2 x = ld_cand(&in[pos < n_in ? pos : n_in - 1]);
-    vb[r] = x.x;
-    idx[r] = (int32_t)x.y;
-    key[r] = float_key(__uint_as_float(x.x));
-    valid |= (pos < n_in && idx[r] >= 0 ? 1u : 0u) << r;
+  // ordered compaction, rank; with R slots per thread, the fewest that hold
+  // the candidates (slot order is position order, so with too many slots per
+  // thread a few candidates would all fall to the first wave).  The smaller
+  // forms are marked unlikely so that the compiler places them out of line.
+  if (__builtin_expect(RM > 1 && n_in <= (int64_t)nthreads, 0)) {
+    merge_full<1>(in, n_in, k, values, indices, nthreads, sm, fs);
+  } else if (__builtin_expect(RM > 4 && n_in <= (int64_t)4 * nthreads, 0)) {
+    merge_full<4>(in, n_in, k, values, indices, nthreads, sm, fs);
+  } else {
+    merge_full<RM>(in, n_in, k, values, indices, nthreads, sm, fs);
   }
-  const SelectRange s = block_select<RM>(key, valid, k, sm);
-  const uint32_t n = block_compact<RM>(key, valid, s, vb, idx, sm,
-                                       [&](uint32_t pos, uint32_t bits, int32_t ix) {
-                                         fs.key[pos] = float_key(__uint_as_float(bits));
-                                         fs.bits[pos] = bits;
-                                         fs.idx[pos] = ix;
-                                       });
-  for (uint32_t i = n + tid; i < ((n + 3u) & ~3u); i += nthreads) {
-    fs.key[i] = 0u;
-    fs.idx[i] = 0x7FFFFFFF;
-  }
-  lds_barrier();
-  rank_and_write(fs, n, k, values, indices);
 }
 
 // Log-sum-exp pairs (Selective Log Softmax page, section "Kernel design":

@@ -214,6 +214,18 @@ def test_small_k_chunk_path_ragged_tails(V, k):
     assert np.array_equal(i, i2)
 
 
+@pytest.mark.parametrize("V,k,C", [(4096, 50, 512), (2048, 256, 512), (2560, 205, 512), (4096, 200, 256),
+                                   (4096, 512, 512), (20000, 300, 1024), (9000, 300, 1024)])
+def test_fused_full_merge_slot_forms(V, k, C):
+    # fewer chunks than k: the last workgroup's merge selects over all
+    # n_chunks * k candidates, with 1, 4 or the full count of slots per
+    # thread depending on how many there are (here from 400 to 9,000, with
+    # the boundaries 1,024 and 4,096 and one above each)
+    x = synthetic.random_logits(2, V, seed=V + k + C, ties=5)
+    v, i = run_select(x, k, C)
+    assert_select_exact(x, v, i, k)
+
+
 def test_fused_merge_counter_is_left_zero_and_workspace_is_shared():
     # A call whose candidates fit one chunk workgroup merges in the last
     # workgroup to finish, counted on the workspace's first word, which every
