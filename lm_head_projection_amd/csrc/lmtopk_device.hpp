@@ -760,6 +760,112 @@ __device__ __forceinline__ void rank_and_write(FinalSmem& fs, uint32_t n, uint32
   }
 }
 
+// Digit (4 bits at `shift`, inverted so that larger keys come first) of the
+// key at position p of a radix-sort pass, and the ballots that group the
+// 64 positions of p's group by digit.
+struct SortDigits {
+  uint32_t d;       // this lane's digit
+  uint64_t valid;   // lanes of the group holding an entry
+  uint64_t b[4];    // lanes whose digit has bit i set
+};
+__device__ __forceinline__ SortDigits sort_digits(uint32_t key, bool ok, int shift) {
+  SortDigits g;
+  g.d = 15u - ((key >> shift) & 15u);
+  g.valid = ballot(ok);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) g.b[i] = ballot(((g.d >> i) & 1u) != 0u);
+  return g;
+}
+// Lanes of the group whose digit is d.
+__device__ __forceinline__ uint64_t sort_peers(const SortDigits& g, uint32_t d) {
+  uint64_t m = g.valid;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m &= ((d >> i) & 1u) ? g.b[i] : ~g.b[i];
+  return m;
+}
+
+// Output order of fs's n entries (1 <= n <= kMaxK, in index order) by a
+// stable least-significant-digit radix sort of their keys, largest first, 4
+// bits per pass over bits [0, hi_bit] (the keys agree above hi_bit; hi_bit <
+// 0: all equal).  Stability keeps equal keys in index order, so the result
+// is (value desc, index asc); then the first min(n, k) are written as
+// rank_and_write does.  Each pass: every group of 64 positions counts its
+// digits with four ballots (lanes 0-15 store the 16 counts), wave 0 turns
+// the [digit][group] counts into exclusive offsets, and every entry moves to
+// its digit's offset plus the number of equal digits before it in its
+// group.  Linear in n, where rank_and_write's counting is quadratic.
+// Scratch inside fs: out_bits is the second key buffer, out_idx the
+// [16][32] count table, rank two 16-bit position buffers; fs.key is
+// overwritten, fs.bits and fs.idx are kept.
+__device__ void sort_and_write(FinalSmem& fs, uint32_t n, uint32_t k, int hi_bit, float* values,
+                               int64_t* indices) {
+  const int lane = lane_id();
+  const uint32_t wave = (uint32_t)wave_id(), nw = blockDim.x >> 6;
+  const uint32_t ng = (n + 63u) >> 6;  // groups of 64 positions, <= 32
+  uint32_t* key_a = fs.key;
+  uint32_t* key_b = fs.out_bits;
+  uint16_t* pos_a = reinterpret_cast<uint16_t*>(fs.rank);
+  uint16_t* pos_b = pos_a + kMaxK;
+  uint32_t* tab = reinterpret_cast<uint32_t*>(fs.out_idx);
+  bool first = true;  // positions are still the identity
+  for (int shift = 0; shift <= hi_bit; shift += 4) {
+    for (uint32_t g = wave; g < ng; g += nw) {
+      const uint32_t p = g * 64u + (uint32_t)lane;
+      const bool ok = p < n;
+      const SortDigits sd = sort_digits(ok ? key_a[p] : 0u, ok, shift);
+      if (lane < 16) tab[lane * 32 + g] = (uint32_t)__popcll(sort_peers(sd, (uint32_t)lane));
+    }
+    lds_barrier();
+    if (wave == 0) {
+      // lane L: table entries [8L, 8L + 8), i.e. digit L / 4, groups 8 (L % 4) + i
+      uint32_t c[8], sum = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t g = (uint32_t)(8 * (lane & 3) + i);
+        c[i] = g < ng ? tab[8 * lane + i] : 0u;
+        sum += c[i];
+      }
+      uint32_t off = wave_scan_inclusive(sum) - sum;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        tab[8 * lane + i] = off;
+        off += c[i];
+      }
+    }
+    lds_barrier();
+    for (uint32_t g = wave; g < ng; g += nw) {
+      const uint32_t p = g * 64u + (uint32_t)lane;
+      const bool ok = p < n;
+      const uint32_t key = ok ? key_a[p] : 0u;
+      const uint32_t pos = first ? p : (ok ? (uint32_t)pos_a[p] : 0u);
+      const SortDigits sd = sort_digits(key, ok, shift);
+      if (ok) {
+        const uint32_t dst = tab[sd.d * 32u + g] + lanes_below(sort_peers(sd, sd.d));
+        key_b[dst] = key;
+        pos_b[dst] = (uint16_t)pos;
+      }
+    }
+    lds_barrier();
+    uint32_t* kt = key_a;
+    key_a = key_b;
+    key_b = kt;
+    uint16_t* pt = pos_a;
+    pos_a = pos_b;
+    pos_b = pt;
+    first = false;
+  }
+  const uint32_t n_out = n < k ? n : k;
+  for (uint32_t r = threadIdx.x; r < n_out; r += blockDim.x) {
+    const uint32_t p = first ? r : (uint32_t)pos_a[r];
+    const uint32_t b = fs.bits[p];
+    const int32_t ix = fs.idx[p];
+    values[r] = __uint_as_float(b);
+    indices[r] = (int64_t)ix;
+    fs.out_bits[r] = b;  // key_a / key_b are no longer read
+    fs.out_idx[r] = ix;
+  }
+}
+
 // Puts this lane's entry into the survivor list if `take`: one LDS atomic per
 // wave reserves the wave's slots; entries past kSurvivorsMax are counted but
 // not stored (the caller then falls back).
@@ -779,6 +885,10 @@ __device__ __forceinline__ void place_survivor(FinalSmem& fs, bool take, uint32_
     fs.idx[p] = ix;
   }
 }
+
+// Above this many selected entries the full path orders them by radix sort
+// (linear) instead of rank counting (quadratic).
+constexpr uint32_t kSortAbove = 256;
 
 // merge_final's full path with R slots per thread (n_in <= R * nthreads):
 // radix select over every candidate (slot order = index order), ordered
@@ -811,6 +921,14 @@ __device__ __forceinline__ void merge_full(const uint2* in, int64_t n_in, uint32
                                          fs.bits[pos] = bits;
                                          fs.idx[pos] = ix;
                                        });
+  if (n > kSortAbove) {
+    // the selected keys lie in [s.prefix, s.kmax], so they agree above the
+    // highest bit in which those two differ
+    const uint32_t span = s.prefix ^ s.kmax;
+    lds_barrier();
+    sort_and_write(fs, n, k, span ? 31 - __clz(span) : -1, values, indices);
+    return;
+  }
   for (uint32_t i = n + tid; i < ((n + 3u) & ~3u); i += nthreads) {
     fs.key[i] = 0u;
     fs.idx[i] = 0x7FFFFFFF;
