@@ -107,10 +107,10 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, int s
     ++lv;
   }
   g->n_levels = lv;
-  // one merge level whose candidates fit the chunk workgroup: its last
-  // workgroup merges instead of a second launch
+  // one merge level whose candidates fit the chunk workgroup, and k up to
+  // kFusedMaxK: its last workgroup merges instead of a second launch
   const int64_t chunk_threads = (int64_t)64 * g->nw;
-  if (lv == 1 && n0 <= chunk_threads * kFusedSlots) {
+  if (lv == 1 && n0 <= chunk_threads * kFusedSlots && k <= kFusedMaxK) {
     g->fused = 1;
     g->n_levels = 0;
   }

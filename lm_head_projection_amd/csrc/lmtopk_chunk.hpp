@@ -72,7 +72,7 @@ __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem
     if (kExtras && f.lse_part != nullptr) have = load_lse_pairs(f.lse_part + (size_t)m * n_part, n_part, pre);
     RowSample rs;
     if (kSample && f.smp.on) rs = load_row_sample(f.smp, m);
-    merge_final<RM>(f.cand + (size_t)m * n_in, n_in, f.heads + (size_t)m * f.n_chunks * kHeads,
+    merge_final<RM, false>(f.cand + (size_t)m * n_in, n_in, f.heads + (size_t)m * f.n_chunks * kHeads,
                     f.n_chunks, f.kc, (uint32_t)f.k, f.values + (size_t)m * f.k,
                     f.indices + (size_t)m * f.k, (int)blockDim.x, sm, fs);
     lds_barrier();  // fs.out_* are complete; fs is reused by the next row

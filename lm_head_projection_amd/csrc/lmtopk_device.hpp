@@ -171,15 +171,24 @@ __device__ __forceinline__ uint2 ld_cand(const uint2* p) {
   return make_uint2((uint32_t)x, (uint32_t)(x >> 32));
 }
 
-// LDS used by one selection (any number of sequential selections may reuse it).
-struct alignas(16) SelectSmem {
-  uint32_t hist[3][256];
+// LDS used by one selection (any number of sequential selections may reuse
+// it).  NC copies of each 256-bin histogram: bin d of copy c is word
+// d * NC + c, and lane l adds into copy l % NC, so that up to NC lanes of a
+// wave with the same digit hit different words (fewer same-word atomics
+// where the digits are skewed); the chunk kernels use one copy (their LDS is
+// mostly the activations), the merge launches four.
+template <int NC>
+struct alignas(16) SelectSmemT {
+  static_assert(NC == 1 || NC == 4, "one or four histogram copies");
+  uint32_t hist[3][256 * NC];
   uint32_t wmin[kMaxWaves];
   uint32_t wmax[kMaxWaves];
   uint32_t wcnt[kMaxWaves];
   uint32_t cgt[kMaxWaves];
   uint32_t ceq[kMaxWaves];
 };
+using SelectSmem = SelectSmemT<1>;
+using MergeSelectSmem = SelectSmemT<4>;
 
 // Outcome of the search: keys k with (k & mask) > prefix are all selected;
 // keys with (k & mask) == prefix are selected in slot order, the first
@@ -195,16 +204,16 @@ struct SelectRange {
 // Block-wide search.  Every thread of the block must call it with its R
 // slots; slot r of lane l in wave w has position (w * R + r) * 64 + l.
 // valid bit r of `valid` marks slot r as a real entry.  k >= 1.
-template <int R>
+template <int R, int NC>
 __device__ SelectRange block_select(const uint32_t (&key)[R], uint32_t valid, uint32_t k,
-                                    SelectSmem& sm) {
+                                    SelectSmemT<NC>& sm) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();
   const int nw = blockDim.x >> 6;
 
   // histogram buffers 0 and 1 start clean; buffer 2 is cleared in pass 0
-  for (int i = tid; i < 512; i += blockDim.x) (&sm.hist[0][0])[i] = 0u;
+  for (int i = tid; i < 512 * NC; i += blockDim.x) (&sm.hist[0][0])[i] = 0u;
 
   uint32_t lmin = 0xFFFFFFFFu, lmax = 0u, cnt = 0u;
 #pragma unroll
@@ -261,12 +270,26 @@ __device__ SelectRange block_select(const uint32_t (&key)[R], uint32_t valid, ui
     uint32_t* hist = sm.hist[pass % 3];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (((valid >> r) & 1u) && ((key[r] & mask) == prefix))
-        atomicAdd(&hist[(key[r] >> shift) & dmask], 1u);
+      if (((valid >> r) & 1u) && ((key[r] & mask) == prefix)) {
+        const uint32_t d = (key[r] >> shift) & dmask;
+        atomicAdd(&hist[NC == 1 ? d : d * NC + (uint32_t)(lane & (NC - 1))], 1u);
+      }
     }
     lds_barrier();
-    // every wave finds the digit of the k-th key on its own
-    const uint4 h = *reinterpret_cast<const uint4*>(&hist[4 * lane]);
+    // every wave finds the digit of the k-th key on its own (lane l: digits
+    // 4l .. 4l + 3)
+    uint4 h;
+    if (NC == 1) {
+      h = *reinterpret_cast<const uint4*>(&hist[4 * lane]);
+    } else {
+      uint32_t c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 q = *reinterpret_cast<const uint4*>(&hist[(4 * lane + i) * NC]);
+        c[i] = q.x + q.y + q.z + q.w;
+      }
+      h = make_uint4(c[0], c[1], c[2], c[3]);
+    }
     const uint32_t s3 = h.w, s2 = h.z + s3, s1 = h.y + s2, s0 = h.x + s1;
     const uint32_t incl = wave_scan_inclusive(s0);
     const uint32_t after = readlane_u32(incl, 63) - incl;  // keys in lanes above this one
@@ -284,7 +307,7 @@ __device__ SelectRange block_select(const uint32_t (&key)[R], uint32_t valid, ui
     const uint32_t above = ge - cnt_eq;
     // clear the buffer two passes ahead (its readers finished before this barrier)
     uint32_t* nxt = sm.hist[(pass + 2) % 3];
-    for (int i = tid; i < 256; i += blockDim.x) nxt[i] = 0u;
+    for (int i = tid; i < 256 * NC; i += blockDim.x) nxt[i] = 0u;
     need -= above;
     prefix |= digit << shift;
     mask |= dmask << shift;
@@ -302,10 +325,10 @@ __device__ SelectRange block_select(const uint32_t (&key)[R], uint32_t valid, ui
 // for each selected slot, pos in [0, selected) following slot order.
 // Returns the number selected (uniform).  vbits[r], index[r] are the payload
 // of slot r.
-template <int R, typename Sink>
+template <int R, int NC, typename Sink>
 __device__ uint32_t block_compact(const uint32_t (&key)[R], uint32_t valid, const SelectRange& s,
                                   const uint32_t (&vbits)[R], const int32_t (&index)[R],
-                                  SelectSmem& sm, Sink&& sink) {
+                                  SelectSmemT<NC>& sm, Sink&& sink) {
   const int lane = lane_id();
   const int wave = wave_id();
   const int nw = blockDim.x >> 6;
@@ -886,16 +909,17 @@ __device__ __forceinline__ void place_survivor(FinalSmem& fs, bool take, uint32_
   }
 }
 
-// Above this many selected entries the full path orders them by radix sort
-// (linear) instead of rank counting (quadratic).
+// Above this many selected entries the full path of a merge launch orders
+// them by radix sort (linear) instead of rank counting (quadratic); the
+// chunk kernels' fused merge handles k <= this and never sorts.
 constexpr uint32_t kSortAbove = 256;
 
 // merge_final's full path with R slots per thread (n_in <= R * nthreads):
 // radix select over every candidate (slot order = index order), ordered
 // compaction, rank and write.
-template <int R>
+template <int R, bool kSort, int NC>
 __device__ __forceinline__ void merge_full(const uint2* in, int64_t n_in, uint32_t k, float* values,
-                                           int64_t* indices, int nthreads, SelectSmem& sm,
+                                           int64_t* indices, int nthreads, SelectSmemT<NC>& sm,
                                            FinalSmem& fs) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -921,7 +945,7 @@ __device__ __forceinline__ void merge_full(const uint2* in, int64_t n_in, uint32
                                          fs.bits[pos] = bits;
                                          fs.idx[pos] = ix;
                                        });
-  if (n > kSortAbove) {
+  if (kSort && n > kSortAbove) {
     // the selected keys lie in [s.prefix, s.kmax], so they agree above the
     // highest bit in which those two differ
     const uint32_t span = s.prefix ^ s.kmax;
@@ -943,7 +967,10 @@ __device__ __forceinline__ void merge_full(const uint2* in, int64_t n_in, uint32
 // blockDim.x * RM).  `heads` (optional) holds each chunk's kHeads best
 // candidates in output order.  Writes the exact top-k sorted by (value desc,
 // index asc) to values / indices, and keeps it in fs.out_bits / fs.out_idx
-// for the token draw (ordered by the caller's next barrier).
+// for the token draw (ordered by the caller's next barrier).  kSort (merge
+// launches): the full path orders more than kSortAbove selected entries by
+// radix sort; without it (the chunk kernels' fused merge, k <= kSortAbove)
+// always by rank counting.
 //
 // Bounded path: a threshold T with at least k chunk maxima >= T is at most
 // the row's k-th largest value (those maxima are k distinct logits), so only
@@ -953,10 +980,10 @@ __device__ __forceinline__ void merge_full(const uint2* in, int64_t n_in, uint32
 // in full.  The survivors (typically a few dozen) go to LDS in any order and
 // are ranked there.  With too many chunks or survivors, the radix select of
 // all candidates runs instead.
-template <int RM>
+template <int RM, bool kSort, int NC>
 __device__ __forceinline__ void merge_final(const uint2* in, int64_t n_in, const uint2* heads, int n_max, int kc,
                             uint32_t k, float* values, int64_t* indices, int nthreads,
-                            SelectSmem& sm, FinalSmem& fs) {
+                            SelectSmemT<NC>& sm, FinalSmem& fs) {
   // nthreads == blockDim.x, passed in so that no load of it queues behind
   // the data loads
   const int tid = threadIdx.x;
@@ -1075,11 +1102,11 @@ __device__ __forceinline__ void merge_final(const uint2* in, int64_t n_in, const
   // thread a few candidates would all fall to the first wave).  The smaller
   // forms are marked unlikely so that the compiler places them out of line.
   if (__builtin_expect(RM > 1 && n_in <= (int64_t)nthreads, 0)) {
-    merge_full<1>(in, n_in, k, values, indices, nthreads, sm, fs);
+    merge_full<1, kSort>(in, n_in, k, values, indices, nthreads, sm, fs);
   } else if (__builtin_expect(RM > 4 && n_in <= (int64_t)4 * nthreads, 0)) {
-    merge_full<4>(in, n_in, k, values, indices, nthreads, sm, fs);
+    merge_full<4, kSort>(in, n_in, k, values, indices, nthreads, sm, fs);
   } else {
-    merge_full<RM>(in, n_in, k, values, indices, nthreads, sm, fs);
+    merge_full<RM, kSort>(in, n_in, k, values, indices, nthreads, sm, fs);
   }
 }
 

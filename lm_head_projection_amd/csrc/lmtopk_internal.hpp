@@ -10,6 +10,11 @@ namespace lmtopk {
 constexpr int kMaxMergeLevels = 8;
 constexpr int64_t kSegMax = 16384;  // candidates one merge workgroup can hold (1024 x 16)
 constexpr int64_t kFusedSlots = 16; // candidate slots per thread of the fused final merge
+// Largest k the chunk launch merges itself: its last workgroup orders the
+// result by rank counting, which is quadratic in k; larger k go to a merge
+// launch, which sorts them (a radix sort kept out of the chunk kernels,
+// whose tail code it would lengthen).
+constexpr int kFusedMaxK = 256;
 
 struct MergeLevel {
   int64_t n_in;  // candidates per row read by this level

@@ -152,12 +152,13 @@ struct MergeArgs {
 // Workgroup (segment s, row m) takes candidates [s*seg, (s+1)*seg) of row m,
 // RM slots per thread (slot order = candidate order = index order), selects
 // their exact top-k and either writes them in index order (intermediate
-// level) or sorts them by (value desc, index asc) through rank counting --
-// each entry's output position is the number of entries ahead of it -- and
-// writes values / indices (final level).
+// level) or sorts them by (value desc, index asc) -- by rank counting (each
+// entry's output position is the number of entries ahead of it) for up to
+// 256 of them, else by a stable radix sort -- and writes values / indices
+// (final level).  Its selection uses four copies of each histogram.
 template <int RM>
 __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
-  __shared__ SelectSmem ssm;
+  __shared__ MergeSelectSmem ssm;
   const int m = blockIdx.y;
   const uint2* in = a.in + (size_t)m * a.n_in;
   if (a.n_seg == 1) {
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
     if (a.lse_part != nullptr) have = load_lse_pairs(a.lse_part + (size_t)m * a.n_part, a.n_part, pre);
     RowSample rs;
     if (a.smp.on) rs = load_row_sample(a.smp, m);
-    merge_final<RM>(in, a.n_in, a.heads ? a.heads + (size_t)m * a.n_max * kHeads : nullptr,
+    merge_final<RM, true>(in, a.n_in, a.heads ? a.heads + (size_t)m * a.n_max * kHeads : nullptr,
                     a.n_max, a.kc, (uint32_t)a.k, a.values + (size_t)m * a.k, a.indices + (size_t)m * a.k,
                     a.threads, ssm, fs);
     lds_barrier();  // ssm is reused; fs.out_* are complete

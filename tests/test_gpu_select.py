@@ -215,12 +215,15 @@ def test_small_k_chunk_path_ragged_tails(V, k):
 
 
 @pytest.mark.parametrize("V,k,C", [(4096, 50, 512), (2048, 256, 512), (2560, 205, 512), (4096, 200, 256),
-                                   (4096, 512, 512), (20000, 300, 1024), (9000, 300, 1024)])
-def test_fused_full_merge_slot_forms(V, k, C):
-    # fewer chunks than k: the last workgroup's merge selects over all
-    # n_chunks * k candidates, with 1, 4 or the full count of slots per
-    # thread depending on how many there are (here from 400 to 9,000, with
-    # the boundaries 1,024 and 4,096 and one above each)
+                                   (20000, 250, 1024), (4096, 512, 512), (20000, 300, 1024),
+                                   (9000, 300, 1024), (16384, 1024, 1024)])
+def test_full_merge_slot_forms(V, k, C):
+    # fewer chunks than k: the merge selects over all n_chunks * k
+    # candidates, with 1, 4 or the full count of slots per thread depending
+    # on how many there are (here from 400 to 16,384, with the boundaries
+    # 1,024 and 4,096 and one above each).  Up to k = 256 the chunk launch's
+    # last workgroup merges and ranks them; above, a merge launch selects and
+    # radix-sorts them.
     x = synthetic.random_logits(2, V, seed=V + k + C, ties=5)
     v, i = run_select(x, k, C)
     assert_select_exact(x, v, i, k)
