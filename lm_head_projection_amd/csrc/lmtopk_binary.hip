@@ -158,7 +158,7 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   __shared__ uint32_t last_wg;
   __shared__ uint32_t task_next;  // kTasks: the next task index to hand out
   HeadStage& hst = csm.hs;
-  head_stage_init(hst);  // ordered by the barriers below
+  head_stage_init<(M >= 2)>(hst);  // ordered by the barriers below
   // from four rows on, the activation bytes and 8-bit dot products (see
   // spread_signs) take fewer instructions than the bit planes
   constexpr bool kBytes = M >= 4 && R == 1;
@@ -593,15 +593,29 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     valid |= (vv ? 1u : 0u) << r;
     if (a.bias == nullptr || !vv) bias_v[r] = 0.f;
   }
+  if constexpr (M == 1) {
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(act_sv), m));
-    float val[R];
+    for (int m = 0; m < M; ++m) {
+      const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(act_sv), m));
+      float val[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) val[r] = fmaf(acc[r][m], s, bias_v[r]);
-    const float zs =
-        kSample ? z_scale(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(temp_v), m))) : 1.f;
-    chunk_select_write<R, kExtras>(val, idx, valid, m, a.out, ssm, hst, m == M - 1, allow[m], zs);
+      for (int r = 0; r < R; ++r) val[r] = fmaf(acc[r][m], s, bias_v[r]);
+      const float zs =
+          kSample ? z_scale(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(temp_v), m))) : 1.f;
+      chunk_select_write<R, kExtras>(val, idx, valid, m, a.out, ssm, hst, m == M - 1, allow[m], zs);
+    }
+  } else {
+    // every row's selection at once (the small-k stages of all rows share
+    // their barriers)
+    float val[M][R], zs[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(act_sv), m));
+#pragma unroll
+      for (int r = 0; r < R; ++r) val[m][r] = fmaf(acc[r][m], s, bias_v[r]);
+      zs[m] = kSample ? z_scale(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(temp_v), m))) : 1.f;
+    }
+    chunk_select_rows<R, M, kExtras>(val, idx, valid, a.out, ssm, hst, allow, zs);
   }
   if (a.out.fused)
     fused_merge_tail<kFusedRM, kExtras, kSample>(fused_merge_of(a.out), ssm, csm.fs, last_wg);

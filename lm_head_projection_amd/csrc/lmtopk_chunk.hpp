@@ -165,6 +165,51 @@ __device__ __forceinline__ uint32_t allowed_bits(const ChunkOut& o, int m, const
   return bits;
 }
 
+// This wave's log-sum-exp pair (max, sum of exp(z - max)) of row m over its
+// valid rows, z = zs * logit; the wave that posts its pair last combines the
+// chunk's pairs (lane w holds wave w's pair) and stores the chunk's pair.  No
+// barrier.
+template <int RPL>
+__device__ __forceinline__ void chunk_lse_pair(const float (&val)[RPL], uint32_t valid, int m,
+                                               const ChunkOut& o, HeadStage& st, float zs) {
+  const size_t row_chunk = (size_t)m * o.n_chunks + blockIdx.x;
+  const int wave = wave_id();
+  const int lane = lane_id();
+  float z[RPL];
+#pragma unroll
+  for (int r = 0; r < RPL; ++r) z[r] = val[r] * zs;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < RPL; ++r)
+    if ((valid >> r) & 1u) mx = fmaxf(mx, z[r]);
+  mx = wave_max_f32(mx);
+  float sum = mx == INFINITY ? 1.f : 0.f;
+  if (mx != INFINITY && mx != -INFINITY) {
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+      if ((valid >> r) & 1u) sum += expf(z[r] - mx);
+  }
+  sum = wave_sum_f32(sum);
+  if (lane == 0) st.lse_w[m][wave] = make_uint2(__float_as_uint(mx), __float_as_uint(sum));
+  // the pair is written before the count (LDS operations of a wave
+  // complete in order; the fence keeps the compiler from reordering)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  uint32_t done = 0u;
+  if (lane == 0) done = atomicAdd(&st.lse_done[m], 1u);
+  done = readlane_u32(done, 0);
+  if (done == (blockDim.x >> 6) - 1u) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    float cm = -INFINITY, cs = 0.f;
+    if (lane < (int)(blockDim.x >> 6)) {
+      const uint2 p = st.lse_w[m][lane];
+      cm = __uint_as_float(p.x);
+      cs = __uint_as_float(p.y);
+    }
+    lse_combine_wave(cm, cs);
+    if (lane == 0) st_cand(&o.lse_part[row_chunk], make_uint2(__float_as_uint(cm), __float_as_uint(cs)));
+  }
+}
+
 // `allow` bit r clear: row r's logit counts as -inf (a disallowed entry).
 // zs: the row's logits are scaled by zs before the normaliser partials (1 /
 // T of a sampled row, else 1); the candidates keep the logits themselves.
@@ -184,47 +229,7 @@ __device__ __forceinline__ void chunk_select_write(const float (&val_in)[RPL], c
     key[r] = float_key(val[r]);
   }
   const size_t row_chunk = (size_t)m * o.n_chunks + blockIdx.x;
-  if (kExtras && o.lse_part != nullptr) {
-    // this wave's log-sum-exp pair (max, sum of exp(z - max)) over its valid
-    // rows, z = zs * logit
-    const int wave = wave_id();
-    const int lane = lane_id();
-    float z[RPL];
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) z[r] = val[r] * zs;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < RPL; ++r)
-      if ((valid >> r) & 1u) mx = fmaxf(mx, z[r]);
-    mx = wave_max_f32(mx);
-    float sum = mx == INFINITY ? 1.f : 0.f;
-    if (mx != INFINITY && mx != -INFINITY) {
-#pragma unroll
-      for (int r = 0; r < RPL; ++r)
-        if ((valid >> r) & 1u) sum += expf(z[r] - mx);
-    }
-    sum = wave_sum_f32(sum);
-    // The chunk's pair: every wave posts its pair; the wave that posts last
-    // combines them (lane w holds wave w's pair) and stores it.
-    if (lane == 0) st.lse_w[m][wave] = make_uint2(__float_as_uint(mx), __float_as_uint(sum));
-    // the pair is written before the count (LDS operations of a wave
-    // complete in order; the fence keeps the compiler from reordering)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    uint32_t done = 0u;
-    if (lane == 0) done = atomicAdd(&st.lse_done[m], 1u);
-    done = readlane_u32(done, 0);
-    if (done == (blockDim.x >> 6) - 1u) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-      float cm = -INFINITY, cs = 0.f;
-      if (lane < (int)(blockDim.x >> 6)) {
-        const uint2 p = st.lse_w[m][lane];
-        cm = __uint_as_float(p.x);
-        cs = __uint_as_float(p.y);
-      }
-      lse_combine_wave(cm, cs);
-      if (lane == 0) st_cand(&o.lse_part[row_chunk], make_uint2(__float_as_uint(cm), __float_as_uint(cs)));
-    }
-  }
+  if (kExtras && o.lse_part != nullptr) chunk_lse_pair<RPL>(val, valid, m, o, st, zs);
   uint2* out = o.cand + row_chunk * o.kc;
   uint2* heads = o.heads + row_chunk * kHeads;
   const int plan = blockIdx.x == (unsigned)o.n_chunks - 1u ? 1 : 0;  // the last chunk may be partial
@@ -256,6 +261,68 @@ __device__ __forceinline__ void chunk_select_write(const float (&val_in)[RPL], c
   // a k < 4 is still a real logit of the row, which the merge may consider)
   block_heads<RPL>(key, valid, vb, idx, st, heads);
   if (!last) lds_barrier();  // the staging is refilled by the next row
+}
+
+// chunk_select_write for rows 0 .. M-1 at once (M >= 2; the binary path):
+// each row's candidates and heads as chunk_select_write writes them, with
+// the small-k selection of all rows between the same two barriers
+// (select_top_rows); rows it leaves (too many staged rows), and every row
+// when k is above the small-k range, take the radix select in turn.
+template <int RPL, int M, bool kExtras = true>
+__device__ __forceinline__ void chunk_select_rows(const float (&val_in)[M][RPL], const int32_t (&idx)[RPL],
+                                                  uint32_t valid, const ChunkOut& o, SelectSmem& sm,
+                                                  HeadStage& st, const uint32_t (&allow)[M],
+                                                  const float (&zs)[M]) {
+  uint32_t key[M][RPL], vb[M][RPL];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float val[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+      val[r] = (!kExtras || ((allow[m] >> r) & 1u)) ? val_in[m][r] : -INFINITY;
+      vb[m][r] = __float_as_uint(val[r]);
+      key[m][r] = float_key(val[r]);
+    }
+    if (kExtras && o.lse_part != nullptr) chunk_lse_pair<RPL>(val, valid, m, o, st, zs[m]);
+  }
+  const int plan = blockIdx.x == (unsigned)o.n_chunks - 1u ? 1 : 0;  // the last chunk may be partial
+  uint32_t n_out[M];
+  const bool small = o.k <= kWaveTops * (int)(blockDim.x >> 6) && o.sel_p[plan] >= 0;
+  if (small) {
+    select_top_rows<M, RPL>(key, valid, vb, idx, (uint32_t)o.k, o.sel_p[plan], o.sel_h[plan], st, n_out,
+                            [&](int m, uint32_t pos, uint32_t bits, int32_t ix) {
+                              const size_t rc = (size_t)m * o.n_chunks + blockIdx.x;
+                              const uint2 e = make_uint2(bits, (uint32_t)ix);
+                              st_cand(&o.cand[rc * o.kc + pos], e);
+                              if (pos < (uint32_t)kHeads) st_cand(&o.heads[rc * kHeads + pos], e);
+                            });
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      if (n_out[m] == 0xFFFFFFFFu) continue;
+      const size_t rc = (size_t)m * o.n_chunks + blockIdx.x;
+      for (int i = (int)n_out[m] + (int)threadIdx.x; i < o.kc; i += blockDim.x)
+        st_cand(&o.cand[rc * o.kc + i], make_uint2(0u, 0xFFFFFFFFu));
+      for (int i = (int)n_out[m] + (int)threadIdx.x; i < kHeads; i += blockDim.x)
+        st_cand(&o.heads[rc * kHeads + i], make_uint2(0u, 0xFFFFFFFFu));
+    }
+  }
+  bool after = false;  // a radix row has run: the next one reuses its LDS
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    if (small && n_out[m] != 0xFFFFFFFFu) continue;
+    if (after) lds_barrier();
+    const size_t rc = (size_t)m * o.n_chunks + blockIdx.x;
+    uint2* out = o.cand + rc * o.kc;
+    const SelectRange s = block_select<RPL>(key[m], valid, (uint32_t)o.k, sm);
+    const uint32_t n = block_compact<RPL>(key[m], valid, s, vb[m], idx, sm,
+                                          [&](uint32_t pos, uint32_t bits, int32_t ix) {
+                                            st_cand(&out[pos], make_uint2(bits, (uint32_t)ix));
+                                          });
+    for (int i = (int)n + (int)threadIdx.x; i < o.kc; i += blockDim.x)
+      st_cand(&out[i], make_uint2(0u, 0xFFFFFFFFu));
+    block_heads<RPL>(key[m], valid, vb[m], idx, st, o.heads + rc * kHeads);
+    after = true;
+  }
 }
 
 // Row m's temperature (1 without a draw; its z_scale is what the normaliser

@@ -433,10 +433,21 @@ struct alignas(16) HeadStage {
   // waves that have posted theirs (zero from head_stage_init on)
   uint2 lse_w[kMaxRows][kMaxWaves];
   uint32_t lse_done[kMaxRows];
+  // select_top_rows (several rows at once): per row the providers' tops and
+  // the scalars above, zero between uses; row m stages into entries
+  // [m * kSmallSurvivorsMax, (m + 1) * kSmallSurvivorsMax) of key .. rank
+  uint32_t rtops[kMaxRows][kMaxWaves * kWaveTops];
+  uint32_t rcount[kMaxRows];
+  uint32_t rtops_done[kMaxRows];
+  uint32_t rthr_ready[kMaxRows];
+  uint32_t rthr[kMaxRows];
 };
+static_assert(kMaxRows * kSmallSurvivorsMax <= kMaxK, "every row's staging fits");
 
-// Puts st in the state select_top_small and block_heads expect on entry;
-// the caller orders it before their first use with a barrier.
+// Puts st in the state select_top_small, select_top_rows (kRows) and
+// block_heads expect on entry; the caller orders it before their first use
+// with a barrier.
+template <bool kRows = false>
 __device__ __forceinline__ void head_stage_init(HeadStage& st) {
   for (int i = threadIdx.x; i < kMaxK; i += blockDim.x) st.rank[i] = 0u;
   if (threadIdx.x == 0) {
@@ -445,6 +456,11 @@ __device__ __forceinline__ void head_stage_init(HeadStage& st) {
     st.thr_ready = 0u;
   }
   if (threadIdx.x < kMaxRows) st.lse_done[threadIdx.x] = 0u;
+  if (kRows && threadIdx.x < kMaxRows) {
+    st.rcount[threadIdx.x] = 0u;
+    st.rtops_done[threadIdx.x] = 0u;
+    st.rthr_ready[threadIdx.x] = 0u;
+  }
 }
 
 // Counting over n entries in LDS, for each entry i < n:
@@ -719,6 +735,148 @@ __device__ uint32_t select_top_small(const uint32_t (&key)[R], uint32_t valid,
     st.thr_ready = 0u;
   }
   return n < k ? n : k;
+}
+
+// select_top_small for rows 0 .. M-1 of a chunk at once (the same P and h
+// for every row): the providers take their tops of every row in turn, the
+// last provider of a row publishes its T, and every wave then stages each
+// row's keys >= T into that row's own part of the staging, so no row waits
+// for another row's barriers; the staged rows of all rows are ranked
+// between the same two barriers.  The result of each row is the one
+// select_top_small gives.  out(m, pos, value_bits, index) is called for
+// pos < n_out[m] = min(k, valid rows); a row with more than
+// kSmallSurvivorsMax staged rows writes nothing, gets n_out[m] =
+// 0xFFFFFFFF and is left to the caller.  st must be as head_stage_init<true>
+// leaves it and is so again on return.
+template <int M, int R, typename Out>
+__device__ void select_top_rows(const uint32_t (&key)[M][R], uint32_t valid,
+                                const uint32_t (&vbits)[M][R], const int32_t (&index)[R],
+                                uint32_t k, int P, int h, HeadStage& st, uint32_t (&n_out)[M],
+                                Out&& out) {
+  static_assert(M <= kMaxRows, "rows per call");
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = wave_id();
+  P = uniform(P);
+  h = uniform(h);
+  const bool stage_all = P == 0;
+
+  // 1. providers: this wave's h largest keys of each row
+  if (!stage_all && wave < P) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      uint32_t left = valid, top = 0u;
+      for (int j = 0; j < h; ++j) {
+        uint32_t best = 0u;
+        int br = 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (((left >> r) & 1u) && key[m][r] > best) {
+            best = key[m][r];
+            br = r;
+          }
+        }
+        const uint32_t wm = wave_max_u32(best);
+        if (lane == j) top = wm;
+        if (wm == 0u) break;
+        const uint64_t holders = ballot(best == wm);
+        if (lane == __ffsll((long long)holders) - 1) left &= ~(1u << br);
+      }
+      if (lane < h) st.rtops[m][wave * h + lane] = top;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+      uint32_t done = 0u;
+      if (lane == 0) done = atomicAdd(&st.rtops_done[m], 1u);
+      done = readlane_u32(done, 0);
+      if (done == (uint32_t)P - 1u) {
+        // the last provider of row m: T = the largest top with at least k
+        // tops >= it
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        const int E = P * h;  // <= 64
+        const uint32_t mine = lane < E ? st.rtops[m][lane] : 0u;
+        uint32_t cnt = 0u;
+        for (int j0 = 0; j0 < E; j0 += 4) {
+          const uint4 q = *reinterpret_cast<const uint4*>(&st.rtops[m][j0]);
+          cnt += (q.x >= mine ? 1u : 0u) + (j0 + 1 < E && q.y >= mine ? 1u : 0u) +
+                 (j0 + 2 < E && q.z >= mine ? 1u : 0u) + (j0 + 3 < E && q.w >= mine ? 1u : 0u);
+        }
+        const uint32_t T = wave_max_u32(lane < E && cnt >= k ? mine : 0u);
+        if (lane == 0) st.rthr[m] = T;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        if (lane == 0) *(volatile lds_t<uint32_t>*)&st.rthr_ready[m] = 1u;
+      }
+    }
+  }
+
+  // 2. each row: wait for its T (bounded, as in select_top_small), stage
+  //    its keys >= T
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    uint32_t ready = 0u;
+    for (int spin = 0; !stage_all && spin < kThresholdSpinMax; ++spin) {
+      ready = uniform(*(volatile lds_t<uint32_t>*)&st.rthr_ready[m]);
+      if (ready) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    uint32_t t = 1u;  // keeps every valid row (real keys are never 0)
+    if (ready) {
+      const uint32_t b = uniform(*(volatile lds_t<uint32_t>*)&st.rthr[m]);
+      if (b != 0u) t = b;
+    }
+    uint64_t sv[R];
+    uint32_t nsv = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      sv[r] = ballot(((valid >> r) & 1u) && key[m][r] >= t);
+      nsv += (uint32_t)__popcll(sv[r]);
+    }
+    if (nsv) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&st.rcount[m], nsv);
+      base = readlane_u32(base, 0);
+      const uint32_t o = (uint32_t)m * kSmallSurvivorsMax;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t p = base + lanes_below(sv[r]);
+        if (((sv[r] >> lane) & 1u) && p < kSmallSurvivorsMax) {
+          st.key[o + p] = key[m][r];
+          st.bits[o + p] = vbits[m][r];
+          st.idx[o + p] = index[r];
+        }
+        base += (uint32_t)__popcll(sv[r]);
+      }
+    }
+  }
+  lds_barrier();
+
+  // 3. rank every row's staged rows, then emit each row's first k
+  uint32_t n[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    n[m] = uniform(st.rcount[m]);
+    const uint32_t o = (uint32_t)m * kSmallSurvivorsMax;
+    if (n[m] <= kSmallSurvivorsMax) rank_count(st.key + o, st.idx + o, n[m], st.rank + o);
+  }
+  lds_barrier();
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint32_t o = (uint32_t)m * kSmallSurvivorsMax;
+    if (n[m] <= kSmallSurvivorsMax) {
+      for (uint32_t i = tid; i < n[m]; i += blockDim.x) {
+        const uint32_t r = st.rank[o + i];
+        if (r < k) out(m, r, st.bits[o + i], st.idx[o + i]);
+        st.rank[o + i] = 0u;
+      }
+      n_out[m] = n[m] < k ? n[m] : k;
+    } else {
+      n_out[m] = 0xFFFFFFFFu;
+    }
+  }
+  if (tid < M) {  // every wave has read them before the barrier above
+    st.rcount[tid] = 0u;
+    st.rtops_done[tid] = 0u;
+    st.rthr_ready[tid] = 0u;
+  }
 }
 
 // LDS of the final merge: up to kMaxK entries to sort (4 slack entries so the

@@ -162,6 +162,26 @@ def test_full_int8_range_including_minus_128(M):
     c.check(50)
 
 
+@pytest.mark.parametrize("M", [2, 5, 8])
+def test_rows_select_independently(M):
+    # The rows' small-k chunk selections share their barriers.  Row 1 has
+    # zero activations, so all its logits are equal: every chunk stages all
+    # of its rows, more than the small-k staging holds, and that row takes
+    # the radix select while the other rows keep the small-k one.  Each row
+    # equals the oracle and, bit for bit, its own result alone (M = 1).
+    H, V = 1024, 20000
+    rng = np.random.default_rng(M)
+    act_q = rng.integers(-128, 128, size=(M, H)).astype(np.int8)
+    act_q[1, :] = 0
+    act_scale = (rng.random(M).astype(np.float32) + 0.5) * np.float32(1e-2)
+    c = Case(M, H, V, seed=11, act=(act_q, act_scale))
+    v, i, _ = c.check(50)
+    assert np.array_equal(i.cpu().numpy()[1], np.arange(50)), "equal logits: the lowest indices"
+    for m in (0, 1, M - 1):
+        v1, i1 = c.run(50, rows=[m])
+        assert torch.equal(i1[0], i[m]) and torch.equal(v1[0].view(torch.int32), v[m].view(torch.int32))
+
+
 # ---------------------------------------------------------------------------
 # config 2: M=2, H=2048, V=32001 (ragged), k=50, planted and duplicate variants
 # ---------------------------------------------------------------------------
