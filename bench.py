@@ -429,19 +429,24 @@ def main():
                                chunk_rows=args.chunk_rows, out=(vals, idx), workspace=work,
                                score_events=ev, lse=lse, sampling=smp, tokens=tokens)
 
-    # auxiliary measurements first (they also bring an idle GPU to its steady
-    # clocks before the timed steps)
+    # auxiliary measurements first: the plain read and copy of 1 GiB (which
+    # sweep the caches and the TLB), then the calls' own auxiliary runs, and
+    # before the warm-up a run of the timed calls themselves, so that the
+    # timed steps start from the state the calls keep in steady decoding
+    # (an idle GPU reaches its steady clocks, and the caches and TLB hold
+    # what the calls use, not what the 1 GiB probes left)
     aux_calls = max(args.steps, 1000)
+    read_gbps = plain_read_gbps(hip, stream, dev)
+    stream_gbps = plain_copy_gbps(hip, stream, dev)
     graph_us = warm_us = None
     if not args.no_aux:
         graph_us = graph_replay_us(args, call, hip, stream, vals, idx)
         # one packed copy only: served from the 256 MB Infinity Cache
         warm_ms, _, _ = time_calls(hip, stream, lambda i, ev: call(i, ev, 1), aux_calls, False)
         warm_us = warm_ms / aux_calls * 1e3
-    read_gbps = plain_read_gbps(hip, stream, dev)
-    stream_gbps = plain_copy_gbps(hip, stream, dev)
     log(f"hipGraph replay {graph_us} us/step; single-copy (cache) {warm_us} us/step; "
         f"plain 1 GiB read {read_gbps:.0f} GB/s, copy {stream_gbps:.0f} GB/s (read + written)")
+    time_calls(hip, stream, call, aux_calls, False)
 
     for i in range(args.warmup):
         call(i, None)
