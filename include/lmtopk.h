@@ -215,7 +215,8 @@ lmtopk_status lmtopk_packed_bytes(int64_t V, int64_t H, int32_t group_size,
    lmtopk_select for these sizes and options.  The same workspace serves all
    three.  It holds a 256-byte completion counter (zero between calls: the
    workgroup that finishes a chunk launch last merges the candidates itself
-   when they fit it, instead of a second launch), then, per row and chunk,
+   when they fit it and k <= 256, instead of a second launch), then, per row
+   and chunk,
    the chunk's four best candidates and all its candidates (8 bytes each),
    plus one intermediate merge level when a row has more than 16384
    candidates, plus 8 bytes per row and chunk for the log-sum-exp pairs.

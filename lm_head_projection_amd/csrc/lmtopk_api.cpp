@@ -58,7 +58,7 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, int s
     // candidates).
     C = V >= 1024 ? 1024 : (int)(g->n_tiles * 64);
     const int64_t n512 = (V + 511) / 512;
-    if (split_ok && V >= 1024 && (V + 1023) / 1024 <= 128 &&
+    if (split_ok && V >= 1024 && (V + 1023) / 1024 <= 128 && k <= kFusedMaxK &&
         n512 * (k < 512 ? k : 512) <= 1024 * kFusedSlots)
       C = 512;
   }

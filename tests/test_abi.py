@@ -79,6 +79,9 @@ def test_workspace_covers_the_two_wave_plan():
     assert lt.binary_plan(1, 40, 128, 40) == (64, 1, 2)
     # the largest activation block (M * H = 65,536) still fits the exchange area
     assert lt.binary_plan(8, 5000, 8192, 50) == (512, 10, 16)
+    # k above the fused merge's range keeps 1,024-row chunks (the merge is a
+    # separate launch either way)
+    assert lt.binary_plan(1, 128256, 4096, 300) == (1024, 126, 16)
     lib = lt._lib
     c = ctypes.c_int32()
     assert lib.lmtopk_binary_plan(1, 1000, 200, 5, None, ctypes.byref(c), ctypes.byref(c),
