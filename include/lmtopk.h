@@ -25,11 +25,12 @@
  *    enqueueing maps to LMTOPK_ERR_HIP; a fault inside a kernel surfaces at
  *    the caller's next synchronisation, as for any asynchronous HIP work.
  *  - The library keeps no state of its own and is thread safe.  The caller's
- *    workspace carries one thing from call to call: a completion counter in
- *    its first 256 bytes, which must be zero before a call starts.  Prepare a
- *    new workspace once with lmtopk_workspace_init (or any zero fill); every
- *    call leaves the counter zero again when it completes and overwrites
- *    whatever else it reads.  Calls that share a workspace must be ordered on
+ *    workspace carries its first 65,792 bytes from call to call: a
+ *    completion counter (256 bytes) and eight per-row key histograms (8 KiB
+ *    each), which must be zero before a call starts.  Prepare a new
+ *    workspace once with lmtopk_workspace_init (or any zero fill); every call
+ *    leaves them zero again when it completes and overwrites whatever else it
+ *    reads.  Calls that share a workspace must be ordered on
  *    one stream; calls that overlap in time need workspaces of their own.
  *  - Inputs must be finite or +-inf.  NaN anywhere is outside the contract and
  *    gives an unspecified (but memory-safe) result.
@@ -215,8 +216,11 @@ lmtopk_status lmtopk_packed_bytes(int64_t V, int64_t H, int32_t group_size,
    lmtopk_select for these sizes and options.  The same workspace serves all
    three.  It holds a 256-byte completion counter (zero between calls: the
    workgroup that finishes a chunk launch last merges the candidates itself
-   when they fit it and k <= 256, instead of a second launch), then, per row
-   and chunk,
+   when they fit it and k <= 256, instead of a second launch) and eight
+   2,048-bin key histograms of 8 KiB (zero between calls: a merge with an
+   intermediate level counts the candidates' keys there, by their top 11
+   bits, and its first level keeps only those in or above the bin of the
+   row's k-th largest), then, per row and chunk,
    the chunk's four best candidates and all its candidates (8 bytes each),
    plus one intermediate merge level when a row has more than 16384
    candidates, plus 8 bytes per row and chunk for the log-sum-exp pairs.
@@ -332,7 +336,7 @@ lmtopk_status lmtopk_select(const float* logits, int64_t M, int64_t V,
  * Calls on one GPU share that array: calls that overlap in time on one GPU
  * (several streams or threads at once) race and give wrong results; order
  * them.  The first call on a GPU also enqueues one small fill kernel on
- * `stream` that clears the array's completion counter.
+ * `stream` that clears the array's completion counter and key histograms.
  * Errors: as lmtopk_binary; WORKSPACE when lmtopk_workspace_bytes for these
  * sizes and options exceeds LMTOPK_NOALLOC_SCRATCH_BYTES.
  */

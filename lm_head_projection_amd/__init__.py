@@ -307,8 +307,9 @@ def workspace_init(workspace):
 
 def new_workspace(M, V, k, chunk_rows=0, device=None):
     """A workspace for these sizes on `device` (default: the current GPU),
-    ready for its first call (zero-filled by workspace_init).  The library keeps its first 256 bytes zero between
-    calls; a workspace passed to the entry points must come from here (or be
+    ready for its first call (zero-filled by workspace_init).  The library
+    keeps its first 65,792 bytes (completion counter and key histograms) zero
+    between calls; a workspace passed to the entry points must come from here (or be
     prepared by workspace_init), and calls that share one must be ordered on
     one stream."""
     if device is None:

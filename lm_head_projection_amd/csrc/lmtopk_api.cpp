@@ -72,7 +72,8 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, int s
   g->n_chunks = (int)((V + C - 1) / C);
   g->kc = k < C ? k : C;
   const int64_t n0 = (int64_t)g->n_chunks * g->kc;
-  g->sync_bytes = 256;
+  g->sync_bytes = kCounterBytes + kHistBytes;
+  static_assert(LMTOPK_MAX_ROWS * kHistBins * 4 == kHistBytes, "one histogram per row");
   g->heads_bytes = round_up((size_t)(M * g->n_chunks * 4 * 8), 256);
   g->region0_bytes = round_up((size_t)(M * n0 * 8), 256);
 
@@ -115,8 +116,11 @@ int make_geometry(int64_t M, int64_t V, int32_t k, int32_t chunk_rows_opt, int s
     g->n_levels = 0;
   }
   g->lse_bytes = round_up((size_t)(M * g->n_chunks * 8), 256);
-  g->workspace_bytes =
-      g->sync_bytes + g->heads_bytes + g->region0_bytes + g->region1_bytes + g->lse_bytes;
+  g->counts_bytes = g->n_levels == 2 && g->level[0].n_seg <= kGatherSegs
+                        ? round_up((size_t)(M * g->level[0].n_seg * 4), 256)
+                        : 0;
+  g->workspace_bytes = g->sync_bytes + g->heads_bytes + g->region0_bytes + g->region1_bytes +
+                       g->lse_bytes + g->counts_bytes;
   return LMTOPK_OK;
 }
 

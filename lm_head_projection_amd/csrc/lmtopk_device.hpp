@@ -1072,11 +1072,19 @@ __device__ __forceinline__ void place_survivor(FinalSmem& fs, bool take, uint32_
 // chunk kernels' fused merge handles k <= this and never sorts.
 constexpr uint32_t kSortAbove = 256;
 
+// Candidate p of a merge's input: in[p] (p clamped into [0, n)).
+struct CandAt {
+  const uint2* in;
+  __device__ __forceinline__ uint2 operator()(int64_t p, int64_t n) const {
+    return ld_cand(&in[p < n ? p : n - 1]);
+  }
+};
+
 // merge_final's full path with R slots per thread (n_in <= R * nthreads):
 // radix select over every candidate (slot order = index order), ordered
-// compaction, rank and write.
-template <int R, bool kSort, int NC>
-__device__ __forceinline__ void merge_full(const uint2* in, int64_t n_in, uint32_t k, float* values,
+// compaction, rank and write.  at(p, n_in) gives candidate p.
+template <int R, bool kSort, int NC, typename At = CandAt>
+__device__ __forceinline__ void merge_full(At at, int64_t n_in, uint32_t k, float* values,
                                            int64_t* indices, int nthreads, SelectSmemT<NC>& sm,
                                            FinalSmem& fs) {
   const int tid = threadIdx.x;
@@ -1090,7 +1098,7 @@ __device__ __forceinline__ void merge_full(const uint2* in, int64_t n_in, uint32
     const int64_t pos = (int64_t)(wave * R + r) * 64 + lane;
     // unconditional (clamped) loads: all R are in flight before the first
     // wait; slots past n_in are marked invalid below
-    const uint2 x = ld_cand(&in[pos < n_in ? pos : n_in - 1]);
+    const uint2 x = at(pos, n_in);
     vb[r] = x.x;
     idx[r] = (int32_t)x.y;
     key[r] = float_key(__uint_as_float(x.x));
@@ -1260,11 +1268,11 @@ __device__ __forceinline__ void merge_final(const uint2* in, int64_t n_in, const
   // thread a few candidates would all fall to the first wave).  The smaller
   // forms are marked unlikely so that the compiler places them out of line.
   if (__builtin_expect(RM > 1 && n_in <= (int64_t)nthreads, 0)) {
-    merge_full<1, kSort>(in, n_in, k, values, indices, nthreads, sm, fs);
+    merge_full<1, kSort>(CandAt{in}, n_in, k, values, indices, nthreads, sm, fs);
   } else if (__builtin_expect(RM > 4 && n_in <= (int64_t)4 * nthreads, 0)) {
-    merge_full<4, kSort>(in, n_in, k, values, indices, nthreads, sm, fs);
+    merge_full<4, kSort>(CandAt{in}, n_in, k, values, indices, nthreads, sm, fs);
   } else {
-    merge_full<RM, kSort>(in, n_in, k, values, indices, nthreads, sm, fs);
+    merge_full<RM, kSort>(CandAt{in}, n_in, k, values, indices, nthreads, sm, fs);
   }
 }
 

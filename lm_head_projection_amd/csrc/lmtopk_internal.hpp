@@ -15,6 +15,20 @@ constexpr int64_t kFusedSlots = 16; // candidate slots per thread of the fused f
 // launch, which sorts them (a radix sort kept out of the chunk kernels,
 // whose tail code it would lengthen).
 constexpr int kFusedMaxK = 256;
+// The workspace starts with the fused merge's completion counter, then one
+// key histogram per row (kHistBins counts of the top 11 bits of the
+// order-preserving key), at offsets that do not depend on the call, so that
+// both stay zero between calls whatever calls share the workspace.  A merge
+// with intermediate levels counts the candidates' keys there first; its
+// first level then keeps only keys in or above the bin of the k-th largest,
+// and its last level sets the row's counts back to zero.
+constexpr size_t kCounterBytes = 256;
+constexpr int kHistBins = 2048;
+constexpr size_t kHistBytes = (size_t)8 * kHistBins * 4;  // LMTOPK_MAX_ROWS rows
+// With two merge levels of at most kGatherSegs segments, the first level
+// writes only its selected candidates and their count per segment, and the
+// last gathers them.
+constexpr int kGatherSegs = 64;
 
 struct MergeLevel {
   int64_t n_in;  // candidates per row read by this level
@@ -62,11 +76,13 @@ struct Geometry {
   int n_levels;    // merge kernel launches (0 when fused)
   int fused;       // the chunk launch's last workgroup does the final merge
   MergeLevel level[kMaxMergeLevels];
-  size_t sync_bytes;     // completion counter of the fused merge (zero between calls)
+  size_t sync_bytes;     // completion counter and key histograms (zero between calls)
   size_t heads_bytes;    // best candidates of each chunk [M][n_chunks][4] x 8 B
   size_t region0_bytes;  // chunk candidates [M][n_chunks * kc] x 8 B
   size_t region1_bytes;  // first intermediate merge output, or 0
   size_t lse_bytes;      // log-sum-exp pairs [M][n_chunks] x (max, sum)
+  size_t counts_bytes;   // two merge levels: the first level's output count
+                         // per row and segment [M][n_seg] x 4 B, or 0
   size_t workspace_bytes;
   float* lse;            // this call's log-sum-exp output [M], or null (not part of the plan)
   const int32_t* allowed;  // this call's bitmask [M][ceil(V/32)], or null (not part of the plan)

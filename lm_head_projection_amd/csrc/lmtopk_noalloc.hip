@@ -13,8 +13,8 @@ namespace lmtopk {
 
 // Every GPU the library runs on holds one copy until the process ends.  Calls
 // on one GPU share it and overlapping calls on one GPU race; each call leaves
-// its completion counter (the first 256 bytes) at zero, which the first use
-// on a device sets up.
+// its completion counter and key histograms (the first kCounterBytes +
+// kHistBytes bytes) at zero, which the first use on a device sets up.
 static __device__ __align__(256) uint8_t scratch[LMTOPK_NOALLOC_SCRATCH_BYTES];
 
 namespace {
@@ -35,7 +35,7 @@ int noalloc_scratch(void** ptr, void* stream) {
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess) return (int)e;
-    const int z = launch_zero(p, 256, stream);
+    const int z = launch_zero(p, kCounterBytes + kHistBytes, stream);
     if (z != 0) return z;
     g_ptr[dev] = p;
   }

@@ -147,7 +147,101 @@ struct MergeArgs {
   int n_part;
   float* lse;             // final: [M] or null
   SampleParams smp;       // final: the token draw (smp.on == 0: none)
+  const uint32_t* hist;   // first of several levels: the rows' key histograms
+                          // [M][kHistBins] (k_hist), or null
+  uint32_t* hist_clear;   // last of several levels: the same, set back to zero
+  uint32_t* counts;       // first of two levels: its output count per row and
+                          // segment [M][n_seg] (then it writes no padding), or null
+  const uint32_t* in_counts;  // last of two levels: those counts, or null
+  int in_seg;                 // ... and the first level's segments (<= kGatherSegs)
 };
+
+// Candidate p of the concatenation of the first level's outputs, segment s
+// holding its count[s] selected candidates at in[s * k]: seg_off (in LDS)
+// holds the exclusive prefix of the counts, n_seg + 1 entries.
+struct GatherAt {
+  const uint2* in;
+  const lds_t<uint32_t>* seg_off;
+  int n_seg;
+  int k;
+  __device__ __forceinline__ uint2 operator()(int64_t p, int64_t n) const {
+    const uint32_t q = (uint32_t)(p < n ? p : n - 1);
+    int lo = 0, hi = n_seg - 1;  // the last segment starting at or before q
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seg_off[mid] <= q) lo = mid;
+      else hi = mid - 1;
+    }
+    return ld_cand(&in[(size_t)lo * k + (q - seg_off[lo])]);
+  }
+};
+
+// Counts of the top 11 bits of the candidates' keys, per row (grid: x = a
+// span of kHistSpan candidates, y = row), added into hist [M][kHistBins],
+// which is zero on entry.  Padding (index -1) is not counted.
+constexpr int kHistSpan = 4096;
+__global__ __launch_bounds__(1024) void k_hist(const uint2* __restrict__ in, int64_t n_in,
+                                               uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[kHistBins];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kHistBins; i += blockDim.x) h[i] = 0u;
+  lds_barrier();
+  const uint2* row = in + (size_t)blockIdx.y * n_in;
+  const int64_t base = (int64_t)blockIdx.x * kHistSpan;
+  for (int i = tid; i < kHistSpan; i += blockDim.x) {
+    const int64_t pos = base + i;
+    if (pos < n_in) {
+      const uint2 x = row[pos];
+      if ((int32_t)x.y >= 0) atomicAdd(&h[float_key(__uint_as_float(x.x)) >> 21], 1u);
+    }
+  }
+  lds_barrier();
+  uint32_t* out = hist + (size_t)blockIdx.y * kHistBins;
+  for (int i = tid; i < kHistBins; i += blockDim.x)
+    if (h[i] != 0u) atomicAdd(&out[i], h[i]);
+}
+
+// The bin of a row's k-th largest key from its histogram: the largest bin b
+// with at least k counted keys in bins >= b (every key of the top k has bin
+// >= b).  Wave 0 finds it (lane l sums bins 32 l .. 32 l + 31) and posts it
+// in *bin; the caller orders it with a barrier.
+__device__ __forceinline__ void kth_bin(const uint32_t* hist, uint32_t k, uint32_t* bin) {
+  if (wave_id() != 0) return;
+  const int lane = lane_id();
+  const uint4* q = reinterpret_cast<const uint4*>(hist + 32 * lane);
+  uint32_t c[32];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint4 v = q[j];
+    c[4 * j] = v.x;
+    c[4 * j + 1] = v.y;
+    c[4 * j + 2] = v.z;
+    c[4 * j + 3] = v.w;
+  }
+  uint32_t sum = 0u;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) sum += c[j];
+  const uint32_t incl = wave_scan_inclusive(sum);
+  const uint32_t above = readlane_u32(incl, 63) - incl;  // keys in the lanes above
+  // the lane whose bins hold the k-th largest: the highest lane with
+  // above + sum >= k (at least k keys in total, or bin 0)
+  const uint64_t have = ballot(above + sum >= k);
+  const int L = have ? 63 - __clzll(have) : 0;
+  uint32_t b = 0u;
+  if (lane == L) {
+    uint32_t acc = above;
+    b = 32u * (uint32_t)lane;
+#pragma unroll
+    for (int j = 31; j >= 0; --j) {
+      acc += c[j];
+      if (acc >= k) {
+        b = 32u * (uint32_t)lane + (uint32_t)j;
+        break;
+      }
+    }
+    *bin = b;
+  }
+}
 
 // Workgroup (segment s, row m) takes candidates [s*seg, (s+1)*seg) of row m,
 // RM slots per thread (slot order = candidate order = index order), selects
@@ -163,14 +257,45 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
   const uint2* in = a.in + (size_t)m * a.n_in;
   if (a.n_seg == 1) {
     __shared__ FinalSmem fs;
+    if (a.hist_clear != nullptr) {  // the first level has read the counts
+      uint4* h = reinterpret_cast<uint4*>(a.hist_clear + (size_t)m * kHistBins);
+      for (int i = threadIdx.x; i < kHistBins / 4; i += blockDim.x) h[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
     uint2 pre[kLsePairs];
     int have = 0;
     if (a.lse_part != nullptr) have = load_lse_pairs(a.lse_part + (size_t)m * a.n_part, a.n_part, pre);
     RowSample rs;
     if (a.smp.on) rs = load_row_sample(a.smp, m);
-    merge_final<RM, true>(in, a.n_in, a.heads ? a.heads + (size_t)m * a.n_max * kHeads : nullptr,
-                    a.n_max, a.kc, (uint32_t)a.k, a.values + (size_t)m * a.k, a.indices + (size_t)m * a.k,
-                    a.threads, ssm, fs);
+    // after two levels, the first level's selected candidates alone,
+    // gathered in segment order (index order), when they fit 4 slots per
+    // thread; else the padded segments
+    __shared__ uint32_t seg_off[kGatherSegs + 1];
+    int64_t total = -1;
+    if (a.in_counts != nullptr) {
+      if (wave_id() == 0) {
+        const int lane = lane_id();
+        const uint32_t c = lane < a.in_seg ? a.in_counts[(size_t)m * a.in_seg + lane] : 0u;
+        const uint32_t incl = wave_scan_inclusive(c);
+        seg_off[lane + 1] = incl;
+        if (lane == 0) seg_off[0] = 0u;
+      }
+      lds_barrier();
+      total = (int64_t)uniform(seg_off[a.in_seg]);
+    }
+    if (total >= 0 && total <= (int64_t)4 * a.threads) {
+      const GatherAt at{in, (const lds_t<uint32_t>*)seg_off, a.in_seg, a.k};
+      float* vo = a.values + (size_t)m * a.k;
+      int64_t* io = a.indices + (size_t)m * a.k;
+      for (int i = threadIdx.x; i < kMaxK + 4; i += blockDim.x) fs.rank[i] = 0u;
+      if (RM == 1 || total <= (int64_t)a.threads)
+        merge_full<1, true>(at, total, (uint32_t)a.k, vo, io, a.threads, ssm, fs);
+      else
+        merge_full<(RM < 4 ? RM : 4), true>(at, total, (uint32_t)a.k, vo, io, a.threads, ssm, fs);
+    } else {
+      merge_final<RM, true>(in, a.n_in, a.heads ? a.heads + (size_t)m * a.n_max * kHeads : nullptr,
+                            a.n_max, a.kc, (uint32_t)a.k, a.values + (size_t)m * a.k,
+                            a.indices + (size_t)m * a.k, a.threads, ssm, fs);
+    }
     lds_barrier();  // ssm is reused; fs.out_* are complete
     float lse = 0.f;
     if (a.lse_part != nullptr)
@@ -186,6 +311,10 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
   const int wave = wave_id();
   const int lane = lane_id();
   const int64_t s0 = (int64_t)blockIdx.x * a.seg;
+  // with the row's key histogram: only keys in or above the bin of the
+  // row's k-th largest can be in its top k
+  __shared__ uint32_t kbin;
+  if (a.hist != nullptr) kth_bin(a.hist + (size_t)m * kHistBins, (uint32_t)a.k, &kbin);
   uint32_t key[RM], vb[RM];
   int32_t idx[RM];
   uint32_t valid = 0u;
@@ -200,12 +329,22 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
     key[r] = float_key(__uint_as_float(e.x));
     valid |= (idx[r] >= 0 ? 1u : 0u) << r;
   }
+  if (a.hist != nullptr) {
+    lds_barrier();
+    const uint32_t b = uniform(kbin);
+#pragma unroll
+    for (int r = 0; r < RM; ++r)
+      if ((key[r] >> 21) < b) valid &= ~(1u << r);
+  }
   const SelectRange s = block_select<RM>(key, valid, (uint32_t)a.k, ssm);
   uint2* out = a.out + ((size_t)m * a.n_seg + blockIdx.x) * a.k;
   const uint32_t n = block_compact<RM>(key, valid, s, vb, idx, ssm,
                                        [&](uint32_t pos, uint32_t bits, int32_t ix) {
                                          out[pos] = make_uint2(bits, (uint32_t)ix);
                                        });
+  // the count lets the last level gather the selected candidates alone;
+  // the padding serves it when there are too many of them for that
+  if (a.counts != nullptr && threadIdx.x == 0) a.counts[(size_t)m * a.n_seg + blockIdx.x] = n;
   for (int i = (int)n + (int)threadIdx.x; i < a.k; i += blockDim.x)
     out[i] = make_uint2(0u, 0xFFFFFFFFu);
 }
@@ -297,10 +436,23 @@ int launch_select_chunks(const Geometry& g, const float* logits, int64_t ld, voi
 int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* indices,
                   void* stream) {
   if (g.fused) return 0;  // the chunk launch merged already
+  uint32_t* hist = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + kCounterBytes);
   uint8_t* ws = static_cast<uint8_t*>(workspace) + g.sync_bytes;
   const uint2* heads = reinterpret_cast<const uint2*>(ws);
   ws += g.heads_bytes;
   uint2* regions[2] = {reinterpret_cast<uint2*>(ws), reinterpret_cast<uint2*>(ws + g.region0_bytes)};
+  const bool counted = g.n_levels >= 2;  // intermediate levels: count the keys first
+  if (counted) {
+    const int64_t n0 = g.level[0].n_in;
+    const dim3 grid((unsigned)((n0 + kHistSpan - 1) / kHistSpan), (unsigned)g.M);
+    const uint2* a_in = regions[0];
+    int64_t a_n = n0;
+    uint32_t* a_h = hist;
+    void* args[] = {&a_in, &a_n, &a_h};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(k_hist), grid, dim3(1024), args, 0,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return (int)e;
+  }
   for (int l = 0; l < g.n_levels; ++l) {
     const MergeLevel& L = g.level[l];
     MergeArgs a;
@@ -322,6 +474,15 @@ int launch_merges(const Geometry& g, void* workspace, float* values, int64_t* in
                      ? reinterpret_cast<const uint2*>(ws + g.region0_bytes + g.region1_bytes)
                      : nullptr;
     a.smp = g.smp;
+    a.hist = counted && l == 0 ? hist : nullptr;
+    a.hist_clear = counted && l == g.n_levels - 1 ? hist : nullptr;
+    // two levels: the first writes counts, the last gathers
+    uint32_t* counts = g.counts_bytes ? reinterpret_cast<uint32_t*>(ws + g.region0_bytes + g.region1_bytes +
+                                                                    g.lse_bytes)
+                                      : nullptr;
+    a.counts = l == 0 ? counts : nullptr;
+    a.in_counts = l == 1 ? counts : nullptr;
+    a.in_seg = g.level[0].n_seg;
     auto kern = merge_kernel(L.rm);
     if (!kern) return (int)hipErrorInvalidValue;
     const hipError_t e = launch1(kern, dim3(L.n_seg, (unsigned)g.M), dim3(64 * L.nw), 0, stream, a);

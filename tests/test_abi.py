@@ -47,13 +47,16 @@ def test_layout_and_sizes():
     assert lt.packed_bytes(32001, 2048) == (32064 * 2048 // 8, 32064 * 16 * 4)
     assert lt.packed_bytes(1, 640) == (64 * 640 // 8, 64 * 8 * 4)   # G=5 pads to 8 scales
     # completion counter (256 B) + chunk heads (243 x 4 x 8 B rounded to 256) + chunk
-    # candidates of the flagship (243 chunks x 50 x 8 B rounded to 256) + log-sum-exp
-    # pairs (243 chunks x 8 B, rounded to 256); one workgroup merges them, no
-    # second region
-    assert lt.workspace_bytes(1, 248320, 50) == 256 + 7936 + 97280 + 2048
-    # k >= chunk rows: every chunk offers all its rows, and the merge needs two levels
-    assert lt.workspace_bytes(8, 248320, 1024) == (256 + 8 * 243 * 32 + 8 * 243 * 1024 * 8
-                                                   + 8 * 16 * 1024 * 8 + 15616)
+    # the completion counter (256 B) and eight key histograms (8 x 2,048 x 4
+    # B), then the heads and candidates of the flagship (243 chunks x 50 x 8 B
+    # rounded to 256) + log-sum-exp pairs (243 chunks x 8 B, rounded to 256);
+    # one workgroup merges them, no second region
+    sync = 256 + 8 * 2048 * 4
+    assert lt.workspace_bytes(1, 248320, 50) == sync + 7936 + 97280 + 2048
+    # k >= chunk rows: every chunk offers all its rows, and the merge needs two
+    # levels (the first level's 16 segments per row also post their counts)
+    assert lt.workspace_bytes(8, 248320, 1024) == (sync + 8 * 243 * 32 + 8 * 243 * 1024 * 8
+                                                   + 8 * 16 * 1024 * 8 + 15616 + 512)
 
 
 def test_workspace_covers_the_two_wave_plan():
@@ -61,8 +64,9 @@ def test_workspace_covers_the_two_wave_plan():
     # so the binary path scores 251 chunks of 512 rows with two waves per tile
     # (16 waves per chunk); the size query covers that plan as well as the
     # other paths' 126 chunks
-    split = 256 + 8192 + 100608 + 2048       # 251 x 4 x 8 -> 8,192; 251 x 50 x 8 -> 100,608;
-    plain = 256 + 4096 + 50432 + 1024        # 251 x 8 -> 2,048 (vs 126 chunks)
+    sync = 256 + 8 * 2048 * 4                 # completion counter, key histograms
+    split = sync + 8192 + 100608 + 2048      # 251 x 4 x 8 -> 8,192; 251 x 50 x 8 -> 100,608;
+    plain = sync + 4096 + 50432 + 1024       # 251 x 8 -> 2,048 (vs 126 chunks)
     assert lt.workspace_bytes(1, 128256, 50) == max(split, plain) == split
     kw = dict(V=128256, H=4096, k=50)
     assert _binary(**kw, ws_bytes=split - 1) == WORKSPACE

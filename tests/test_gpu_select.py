@@ -229,6 +229,22 @@ def test_full_merge_slot_forms(V, k, C):
     assert_select_exact(x, v, i, k)
 
 
+@pytest.mark.parametrize("V", [40000, 80000])
+def test_two_level_merge_with_key_histogram(V):
+    # k = 1,024 over all rows of 1,024-row chunks: the merge counts the keys
+    # first, its first level keeps the keys in or above the bin of the k-th
+    # largest, and the last level gathers what the segments kept (row 0)
+    # unless that is more than 4 slots per thread (row 1: all logits equal,
+    # every segment keeps k, 5 segments at V = 80,000) and reads the padded
+    # segments instead
+    x = synthetic.random_logits(3, V, seed=V, ties=3)
+    x[1, :] = np.float32(0.25)
+    x[2, : V // 2] = np.float32(-1.0)  # half of row 2 equal, below the rest
+    v, i = run_select(x, 1024, 1024)
+    assert_select_exact(x, v, i, 1024)
+    assert np.array_equal(i[1], np.arange(1024))
+
+
 def test_fused_merge_counter_is_left_zero_and_workspace_is_shared():
     # A call whose candidates fit one chunk workgroup merges in the last
     # workgroup to finish, counted on the workspace's first word, which every
@@ -242,5 +258,5 @@ def test_fused_merge_counter_is_left_zero_and_workspace_is_shared():
     for k in (50, 1024, 7, 50, 1024, 50):
         v, i = lt.topk_logits(t, k, workspace=ws)
         torch.cuda.synchronize()
-        assert int(ws[:256].count_nonzero()) == 0, f"completion counter not reset after k={k}"
+        assert int(ws[:65792].count_nonzero()) == 0, f"counter / key histograms not zero after k={k}"
         assert_select_exact(x, v.cpu().numpy(), i.cpu().numpy(), k)
