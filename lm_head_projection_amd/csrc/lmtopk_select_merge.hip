@@ -203,20 +203,28 @@ __global__ __launch_bounds__(1024) void k_hist(const uint2* __restrict__ in, int
 
 // The bin of a row's k-th largest key from its histogram: the largest bin b
 // with at least k counted keys in bins >= b (every key of the top k has bin
-// >= b).  Wave 0 finds it (lane l sums bins 32 l .. 32 l + 31) and posts it
-// in *bin; the caller orders it with a barrier.
-__device__ __forceinline__ void kth_bin(const uint32_t* hist, uint32_t k, uint32_t* bin) {
-  if (wave_id() != 0) return;
+// >= b).  Wave 0 finds it from q, its lane l's bins 32 l .. 32 l + 31 (as
+// kth_bin_load reads them), and posts it in *bin; the caller orders it with
+// a barrier.
+struct HistSlice {
+  uint4 q[8];
+};
+__device__ __forceinline__ HistSlice kth_bin_load(const uint32_t* hist) {
+  HistSlice h;
+  const uint4* p = reinterpret_cast<const uint4*>(hist + 32 * lane_id());
+#pragma unroll
+  for (int j = 0; j < 8; ++j) h.q[j] = p[j];
+  return h;
+}
+__device__ __forceinline__ void kth_bin(const HistSlice& h, uint32_t k, uint32_t* bin) {
   const int lane = lane_id();
-  const uint4* q = reinterpret_cast<const uint4*>(hist + 32 * lane);
   uint32_t c[32];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint4 v = q[j];
-    c[4 * j] = v.x;
-    c[4 * j + 1] = v.y;
-    c[4 * j + 2] = v.z;
-    c[4 * j + 3] = v.w;
+    c[4 * j] = h.q[j].x;
+    c[4 * j + 1] = h.q[j].y;
+    c[4 * j + 2] = h.q[j].z;
+    c[4 * j + 3] = h.q[j].w;
   }
   uint32_t sum = 0u;
 #pragma unroll
@@ -227,10 +235,9 @@ __device__ __forceinline__ void kth_bin(const uint32_t* hist, uint32_t k, uint32
   // above + sum >= k (at least k keys in total, or bin 0)
   const uint64_t have = ballot(above + sum >= k);
   const int L = have ? 63 - __clzll(have) : 0;
-  uint32_t b = 0u;
   if (lane == L) {
     uint32_t acc = above;
-    b = 32u * (uint32_t)lane;
+    uint32_t b = 32u * (uint32_t)lane;
 #pragma unroll
     for (int j = 31; j >= 0; --j) {
       acc += c[j];
@@ -311,10 +318,13 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
   const int wave = wave_id();
   const int lane = lane_id();
   const int64_t s0 = (int64_t)blockIdx.x * a.seg;
-  // with the row's key histogram: only keys in or above the bin of the
-  // row's k-th largest can be in its top k
   __shared__ uint32_t kbin;
-  if (a.hist != nullptr) kth_bin(a.hist + (size_t)m * kHistBins, (uint32_t)a.k, &kbin);
+  // with the row's key histogram: only keys in or above the bin of the
+  // row's k-th largest can be in its top k (wave 0 reads the counts before
+  // its candidates, so both are in flight together)
+  const bool counted = a.hist != nullptr;
+  HistSlice hs;
+  if (counted && wave == 0) hs = kth_bin_load(a.hist + (size_t)m * kHistBins);
   uint32_t key[RM], vb[RM];
   int32_t idx[RM];
   uint32_t valid = 0u;
@@ -329,7 +339,8 @@ __global__ __launch_bounds__(1024) void k_merge(MergeArgs a) {
     key[r] = float_key(__uint_as_float(e.x));
     valid |= (idx[r] >= 0 ? 1u : 0u) << r;
   }
-  if (a.hist != nullptr) {
+  if (counted) {
+    if (wave == 0) kth_bin(hs, (uint32_t)a.k, &kbin);
     lds_barrier();
     const uint32_t b = uniform(kbin);
 #pragma unroll
