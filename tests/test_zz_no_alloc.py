@@ -54,7 +54,8 @@ def test_noalloc_matches_the_workspace_entry_point():
     f = _fn()
     big = (4, 2048, 60001, 100)
     small = (1, 1024, 20001, 10)
-    for (M, H, V, k), seed in ((big, 1), (small, 2)):
+    two_levels = (2, 1024, 60001, 512)  # 59 x 512 candidates per row: the key histogram
+    for (M, H, V, k), seed in ((big, 1), (small, 2), (two_levels, 3)):
         case = _case(M, H, V, seed)
         lse_a = torch.empty(M, device="cuda")
         lse_b = torch.empty(M, device="cuda")
