@@ -233,7 +233,7 @@ __device__ __forceinline__ void chunk_select_write(const float (&val_in)[RPL], c
   uint2* out = o.cand + row_chunk * o.kc;
   uint2* heads = o.heads + row_chunk * kHeads;
   const int plan = blockIdx.x == (unsigned)o.n_chunks - 1u ? 1 : 0;  // the last chunk may be partial
-  if (o.k <= kWaveTops * (int)(blockDim.x >> 6) && o.sel_p[plan] >= 0) {
+  if (o.sel_p[plan] >= 0) {  // small k: the plan's P * h <= 64 tops cover it
     const uint32_t n = select_top_small<RPL>(key, valid, vb, idx, (uint32_t)o.k, o.sel_p[plan],
                                              o.sel_h[plan], st,
                                              [&](uint32_t pos, uint32_t bits, int32_t ix) {
@@ -287,7 +287,7 @@ __device__ __forceinline__ void chunk_select_rows(const float (&val_in)[M][RPL],
   }
   const int plan = blockIdx.x == (unsigned)o.n_chunks - 1u ? 1 : 0;  // the last chunk may be partial
   uint32_t n_out[M];
-  const bool small = o.k <= kWaveTops * (int)(blockDim.x >> 6) && o.sel_p[plan] >= 0;
+  const bool small = o.sel_p[plan] >= 0;
   if (small) {
     select_top_rows<M, RPL>(key, valid, vb, idx, (uint32_t)o.k, o.sel_p[plan], o.sel_h[plan], st, n_out,
                             [&](int m, uint32_t pos, uint32_t bits, int32_t ix) {

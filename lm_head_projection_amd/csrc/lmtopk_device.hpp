@@ -381,7 +381,8 @@ __device__ uint32_t block_compact(const uint32_t (&key)[R], uint32_t valid, cons
 // its heads.
 constexpr int kHeads = 4;
 
-// Small-k chunk selection (select_top_small) takes this many keys per wave.
+// Small-k chunk selection (select_top_small): its providers' tops number at
+// most kMaxWaves * kWaveTops = 64 (so k <= 64).
 constexpr int kWaveTops = 4;
 // ... and gives up (the radix select runs) above this many survivors.
 constexpr uint32_t kSmallSurvivorsMax = 256;
@@ -599,7 +600,7 @@ using lds_t = __attribute__((address_space(3))) T;
 // sleep each; the wave that publishes it never waits for anything).
 constexpr int kThresholdSpinMax = 1 << 22;
 
-// Exact top-k of one chunk row for small k (k <= kWaveTops * waves), without
+// Exact top-k of one chunk row for small k (a plan of P * h <= 64 tops), without
 // radix passes.  The first P waves (the "providers", all of whose rows are
 // valid; `small_select_plan`) each take their h largest keys; the provider
 // that completes this set finds T, the k-th largest of the P h tops, alone
