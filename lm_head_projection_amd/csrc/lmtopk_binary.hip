@@ -618,7 +618,8 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     chunk_select_rows<R, M, kExtras>(val, idx, valid, a.out, ssm, hst, allow, zs);
   }
   if (a.out.fused)
-    fused_merge_tail<kFusedRM, kExtras, kSample>(fused_merge_of(a.out), ssm, csm.fs, last_wg);
+    fused_merge_tail<kFusedRM, kExtras, kSample, (M >= 2 ? M : 0)>(fused_merge_of(a.out), ssm, csm.fs,
+                                                                   last_wg);
 }
 namespace {
 

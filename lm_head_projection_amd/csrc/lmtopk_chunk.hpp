@@ -49,7 +49,11 @@ struct FusedMerge {
 // drawn right after its merge (sample_row).
 // kExtras false: the launch has no log-sum-exp output or bitmask; kSample
 // false: no draw; that code is left out.
-template <int RM, bool kExtras = true, bool kSample = true>
+// kRows (compile-time rows, 2 or more, and no extras): the rows' bounded
+// merges run side by side, each by its own group of waves
+// (merge_rows_grouped); rows it leaves, and every row where the sizes do
+// not allow it, are merged one after another as for one row.
+template <int RM, bool kExtras = true, bool kSample = true, int kRows = 0>
 __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem& sm, FinalSmem& fs,
                                  uint32_t& last) {
   // every store of this thread has been acknowledged (gfx9 counts stores in vmcnt)
@@ -64,6 +68,29 @@ __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem
   if (uniform(last) == 0u) return;
   const int64_t n_in = (int64_t)f.n_chunks * f.kc;
   const int n_part = f.n_chunks;  // one log-sum-exp pair per chunk and row
+  if constexpr (kRows >= 2 && !kExtras && !kSample) {
+    constexpr int G = kMaxWaves / kRows;  // waves per row
+    if ((int)(blockDim.x >> 6) >= kRows * G &&
+        merge_bounded(f.heads, f.n_chunks, (uint32_t)f.k, kMaxWaves * 64)) {
+      if (threadIdx.x < (unsigned)kMaxRows) {
+        fs.g_sync[threadIdx.x] = 0u;
+        fs.g_done[threadIdx.x] = 0u;
+      }
+      lds_barrier();
+      merge_rows_grouped<kRows, G>(f.cand, n_in, f.heads, f.n_chunks, f.kc, (uint32_t)f.k, f.values,
+                                   f.indices, fs);
+      lds_barrier();
+      for (int m = 0; m < kRows; ++m) {
+        if (uniform(fs.g_done[m])) continue;
+        merge_final<RM, false>(f.cand + (size_t)m * n_in, n_in, f.heads + (size_t)m * f.n_chunks * kHeads,
+                               f.n_chunks, f.kc, (uint32_t)f.k, f.values + (size_t)m * f.k,
+                               f.indices + (size_t)m * f.k, (int)blockDim.x, sm, fs);
+        lds_barrier();  // fs is reused by the next row
+      }
+      if (threadIdx.x == 0) __hip_atomic_store(f.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+  }
   for (int m = 0; m < f.M; ++m) {
     // the row's log-sum-exp partials and draw parameters are requested
     // before the merge, which waits for its own loads meanwhile

@@ -74,6 +74,7 @@ __device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, kCtrl, kRowMask, 0xF, kBoundZero);
 }
 constexpr int kQuadBcast0 = 0x00;    // quad_perm [0,0,0,0]
+constexpr int kQuadBcast3 = 0xFF;    // quad_perm [3,3,3,3]
 constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;
@@ -478,13 +479,15 @@ __device__ __forceinline__ void head_stage_init(HeadStage& st) {
 // key and idx must be readable up to index 16 * ceil(n / 16) (entries past
 // n are not counted); rank[0, n) must be zero on entry; the caller orders
 // the result with a barrier.
+// (wave, nw: this wave's place among the waves sharing the jobs, by default
+// the whole workgroup.)
 template <bool kAhead = true>
 __device__ __forceinline__ void rank_count(const uint32_t* key, const int32_t* idx, uint32_t n,
-                                           uint32_t* rank) {
+                                           uint32_t* rank, uint32_t wave = (uint32_t)wave_id(),
+                                           uint32_t nw = blockDim.x >> 6) {
   n = uniform(n);
   if (n == 0u) return;
   const int lane = lane_id();
-  const uint32_t wave = (uint32_t)wave_id(), nw = blockDim.x >> 6;
   const uint32_t nb = (n + 63u) >> 6;
   const uint32_t ns = (n + 15u) >> 4;
   // job = (slice, block), spread over every wave
@@ -895,9 +898,16 @@ struct alignas(16) FinalSmem {
   uint32_t wmax[kMaxWaves];
   uint32_t hist[256];  // chunk maxima per 8-bit digit
   // the row's result in output order, kept for the token draw
-  uint32_t out_bits[kMaxK];
-  int32_t out_idx[kMaxK];
+  // (16-byte aligned: merge_rows_grouped keeps histograms there)
+  alignas(16) uint32_t out_bits[kMaxK];
+  alignas(16) int32_t out_idx[kMaxK];
   uint2 lse_w[kMaxWaves];  // merge_lse: each wave's log-sum-exp pair
+  // merge_rows_grouped: per group (row) its barrier counter, survivor and
+  // over-chunk counts and outcome
+  uint32_t g_sync[kMaxRows];
+  uint32_t g_count[kMaxRows];
+  uint32_t g_over[kMaxRows];
+  uint32_t g_done[kMaxRows];
 };
 
 // Entries [0, n) of fs are filled, [n, 4 * ceil(n / 4)) hold padding that is
@@ -1126,6 +1136,184 @@ __device__ __forceinline__ void merge_full(At at, int64_t n_in, uint32_t k, floa
   }
   lds_barrier();
   rank_and_write(fs, n, k, values, indices);
+}
+
+// Whether merge_final takes its bounded path for these sizes (with nthreads
+// threads, one head each).
+__device__ __forceinline__ bool merge_bounded(const uint2* heads, int n_max, uint32_t k, int nthreads) {
+  return heads != nullptr && n_max >= (int)k && n_max <= 256 && n_max * kHeads <= nthreads;
+}
+
+// Barrier of the `waves` waves of one group (not the whole workgroup): each
+// wave counts itself on the group's LDS counter and waits until the count
+// reaches target + waves (bounded, as every wait here; the waves of a
+// workgroup are all resident, so the count always gets there).
+__device__ __forceinline__ void group_sync(uint32_t* ctr, uint32_t waves, uint32_t& target) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  target += waves;
+  if (lane_id() == 0) atomicAdd(ctr, 1u);
+  for (int spin = 0; spin < kThresholdSpinMax; ++spin) {
+    if (uniform(*(volatile lds_t<uint32_t>*)ctr) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// merge_final's bounded path for rows 0 .. M-1 at once: row g is merged by
+// waves [g G, (g + 1) G) with barriers of their own (group_sync), so the
+// rows' merges overlap instead of following one another.  Same T,
+// survivors, ranks and outputs as merge_final; a group's LDS is the part g
+// of fs's arrays (survivors: 256 entries of key .. rank, maxima histogram:
+// out_bits, over-chunk list: out_idx).  Requires merge_bounded() for the
+// sizes and M * G <= waves.  Row g's outcome is fs.g_done[g] = 1 when
+// written, 0 when it has more than 256 survivors (the caller then merges it
+// with merge_final); ordered by the caller's next workgroup barrier.
+constexpr uint32_t kGroupSurvivors = 256;
+template <int M, int G>
+__device__ void merge_rows_grouped(const uint2* cand, int64_t n_in, const uint2* heads, int n_max, int kc,
+                                   uint32_t k, float* values, int64_t* indices, FinalSmem& fs) {
+  static_assert(M * G <= kMaxWaves && G >= 2 && M * kGroupSurvivors <= kMaxK, "groups");
+  constexpr int S = 64 * G;  // threads per group
+  constexpr int J = (kMaxWaves * kHeads * 16 + S - 1) / S;  // heads per thread (n_heads <= 1024)
+  const int wave = wave_id();
+  const int lane = lane_id();
+  const int g = wave / G;
+  if (g >= M) return;
+  const int gw = wave - g * G;
+  const int t = gw * 64 + lane;
+  const int n_heads = n_max * kHeads;
+  const uint2* hrow = heads + (size_t)g * n_heads;
+  const uint2* crow = cand + (size_t)g * n_in;
+  uint32_t* skey = fs.key + g * kGroupSurvivors;
+  uint32_t* sbits = fs.bits + g * kGroupSurvivors;
+  int32_t* sidx = fs.idx + g * kGroupSurvivors;
+  uint32_t* srank = fs.rank + g * kGroupSurvivors;
+  uint32_t* hist = fs.out_bits + g * 256;
+  int32_t* over_list = fs.out_idx + g * 256;
+  uint32_t* ctr = &fs.g_sync[g];
+  uint32_t target = 0u;
+
+  // every head of the row, J per thread (head e = t + j S; the four heads of
+  // a chunk sit in one quad of lanes), all loads in flight at once
+  uint32_t hb[J];
+  int32_t hx[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int e = t + j * S;
+    const uint2 x = ld_cand(&hrow[e < n_heads ? e : n_heads - 1]);
+    hb[j] = x.x;
+    hx[j] = e < n_heads ? (int32_t)x.y : -1;
+  }
+  for (int i = t; i < 256; i += S) hist[i] = 0u;
+  for (int i = t; i < (int)kGroupSurvivors; i += S) srank[i] = 0u;
+  if (t == 0) {
+    fs.g_count[g] = 0u;
+    fs.g_over[g] = 0u;
+  }
+  // the chunk maxima (first lane of each quad): shared high bits
+  const bool q0 = (lane & 3) == 0;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (q0 && hx[j] >= 0) {
+      const uint32_t kj = float_key(__uint_as_float(hb[j]));
+      lo = min(lo, kj);
+      hi = max(hi, kj);
+    }
+  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
+  if (lane == 0) {
+    fs.wmin[wave] = lo;
+    fs.wmax[wave] = hi;
+  }
+  group_sync(ctr, G, target);
+  const uint32_t gmin = wave_min_u32(lane < G ? fs.wmin[g * G + lane] : 0xFFFFFFFFu);
+  const uint32_t gmax = wave_max_u32(lane < G ? fs.wmax[g * G + lane] : 0u);
+  // T as merge_final finds it: one histogram of the maxima's next 8 bits
+  uint32_t t_key = gmin;
+  if (gmin != gmax) {
+    const int top = 31 - __clz(gmin ^ gmax);
+    const int shift = top >= 7 ? top - 7 : 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (q0 && hx[j] >= 0) atomicAdd(&hist[(float_key(__uint_as_float(hb[j])) >> shift) & 0xFFu], 1u);
+    group_sync(ctr, G, target);
+    const uint4 h = *reinterpret_cast<const uint4*>(&hist[4 * lane]);
+    const uint32_t s3 = h.w, s2 = h.z + s3, s1 = h.y + s2, s0 = h.x + s1;
+    const uint32_t incl = wave_scan_inclusive(s0);
+    const uint32_t after = readlane_u32(incl, 63) - incl;
+    const uint64_t have = ballot(s0 + after >= k);
+    const int L = 63 - __clzll(have);
+    const uint32_t i_star = s3 + after >= k ? 3u : s2 + after >= k ? 2u : s1 + after >= k ? 1u : 0u;
+    const uint32_t digit = 4u * (uint32_t)L + readlane_u32(i_star, L);
+    const uint32_t low = shift + 8 >= 32 ? 0xFFFFFFFFu : (1u << (shift + 8)) - 1u;
+    t_key = (gmax & ~low) | (digit << shift);
+  }
+  // survivors: heads >= T of chunks whose last head is below T; the other
+  // chunks ("over") may hold survivors beyond their heads
+  auto place = [&](bool take, uint32_t kx, uint32_t bits, int32_t ix) {
+    const uint64_t b = ballot(take);
+    if (b == 0u) return;
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&fs.g_count[g], (uint32_t)__popcll(b));
+    base = readlane_u32(base, 0);
+    const uint32_t p = base + lanes_below(b);
+    if (take && p < kGroupSurvivors) {
+      skey[p] = kx;
+      sbits[p] = bits;
+      sidx[p] = ix;
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t kj = float_key(__uint_as_float(hb[j]));
+    const uint32_t last_in = (lane & 3) == 3 && kc > kHeads && hx[j] >= 0 && kj >= t_key ? 1u : 0u;
+    const bool over = dpp<kQuadBcast3>(0u, last_in) != 0u;
+    place(hx[j] >= 0 && !over && kj >= t_key, kj, hb[j], hx[j]);
+    const uint64_t bo = ballot(q0 && over);
+    if (bo != 0u) {
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&fs.g_over[g], (uint32_t)__popcll(bo));
+      base = readlane_u32(base, 0);
+      if (q0 && over) over_list[base + lanes_below(bo)] = (t + j * S) >> 2;
+    }
+  }
+  group_sync(ctr, G, target);
+  const uint32_t n_over = uniform(fs.g_over[g]);
+  if (n_over) {  // rare: those chunks' candidate lists in full
+    const uint32_t total = n_over * (uint32_t)kc;
+    for (uint32_t base = 0; base < total; base += S) {
+      const uint32_t i = base + (uint32_t)t;
+      bool take = false;
+      uint2 x = make_uint2(0u, 0xFFFFFFFFu);
+      uint32_t kx = 0u;
+      if (i < total) {
+        x = ld_cand(&crow[(int64_t)over_list[i / (uint32_t)kc] * kc + i % (uint32_t)kc]);
+        kx = float_key(__uint_as_float(x.x));
+        take = (int32_t)x.y >= 0 && kx >= t_key;
+      }
+      place(take, kx, x.x, (int32_t)x.y);
+    }
+    group_sync(ctr, G, target);
+  }
+  const uint32_t n = uniform(fs.g_count[g]);
+  if (n > kGroupSurvivors) {
+    if (t == 0) fs.g_done[g] = 0u;
+    return;
+  }
+  rank_count(skey, sidx, n, srank, (uint32_t)gw, (uint32_t)G);
+  group_sync(ctr, G, target);
+  float* vo = values + (size_t)g * k;
+  int64_t* io = indices + (size_t)g * k;
+  for (uint32_t i = t; i < n; i += S) {
+    const uint32_t r = srank[i];
+    if (r < k) {
+      vo[r] = __uint_as_float(sbits[i]);
+      io[r] = (int64_t)sidx[i];
+    }
+  }
+  if (t == 0) fs.g_done[g] = 1u;
 }
 
 // Final merge of one row.  `in` holds the n_in candidates of the n_max chunks
