@@ -49,10 +49,11 @@ struct FusedMerge {
 // drawn right after its merge (sample_row).
 // kExtras false: the launch has no log-sum-exp output or bitmask; kSample
 // false: no draw; that code is left out.
-// kRows (compile-time rows, 2 or more, and no extras): the rows' bounded
+// kRows (compile-time rows, 2 or more, and no draw): the rows' bounded
 // merges run side by side, each by its own group of waves
-// (merge_rows_grouped); rows it leaves, and every row where the sizes do
-// not allow it, are merged one after another as for one row.
+// (merge_rows_grouped), and then each row's log-sum-exp by the first wave of
+// its group; rows it leaves, and every row where the sizes do not allow it,
+// are merged one after another as for one row.
 template <int RM, bool kExtras = true, bool kSample = true, int kRows = 0>
 __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem& sm, FinalSmem& fs,
                                  uint32_t& last) {
@@ -68,10 +69,18 @@ __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem
   if (uniform(last) == 0u) return;
   const int64_t n_in = (int64_t)f.n_chunks * f.kc;
   const int n_part = f.n_chunks;  // one log-sum-exp pair per chunk and row
-  if constexpr (kRows >= 2 && !kExtras && !kSample) {
+  if constexpr (kRows >= 2 && !kSample) {
     constexpr int G = kMaxWaves / kRows;  // waves per row
     if ((int)(blockDim.x >> 6) >= kRows * G &&
         merge_bounded(f.heads, f.n_chunks, (uint32_t)f.k, kMaxWaves * 64)) {
+      // the first wave of each group requests its row's log-sum-exp pairs
+      // (n_chunks <= 64 * kLsePairs here) before the merge
+      const int wave = wave_id();
+      const int row = wave / G;
+      const bool lse_lead = kExtras && f.lse_part != nullptr && row < kRows && wave == row * G;
+      uint2 pre[kLsePairs];
+      const uint2* lse_row = lse_lead ? f.lse_part + (size_t)row * n_part : f.lse_part;
+      if (kExtras) load_lse_pairs_wave(lse_row, n_part, lse_lead, pre);
       if (threadIdx.x < (unsigned)kMaxRows) {
         fs.g_sync[threadIdx.x] = 0u;
         fs.g_done[threadIdx.x] = 0u;
@@ -79,6 +88,7 @@ __device__ __forceinline__ void fused_merge_tail(const FusedMerge& f, SelectSmem
       lds_barrier();
       merge_rows_grouped<kRows, G>(f.cand, n_in, f.heads, f.n_chunks, f.kc, (uint32_t)f.k, f.values,
                                    f.indices, fs);
+      if (kExtras && lse_lead) lse_wave(pre, f.lse ? f.lse + row : nullptr);
       lds_barrier();
       for (int m = 0; m < kRows; ++m) {
         if (uniform(fs.g_done[m])) continue;

@@ -1512,6 +1512,38 @@ __device__ __forceinline__ int load_lse_pairs(const uint2* part, int n, uint2 (&
   return mode;
 }
 
+// Mode 1 by any one wave: lane l holds the pairs l + 64 j of the row (absent
+// ones (-inf, 0)); every lane of the wave returns the result and lane 0
+// stores it to *out (unless out is null).
+__device__ __forceinline__ float lse_wave(const uint2 (&pre)[kLsePairs], float* out) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kLsePairs; ++j) mx = fmaxf(mx, __uint_as_float(pre[j].x));
+  const float M = wave_max_f32(mx);
+  float sum = 0.f;
+  if (M != INFINITY && M != -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < kLsePairs; ++j) {
+      const float pm = __uint_as_float(pre[j].x);
+      if (pm != -INFINITY) sum += __uint_as_float(pre[j].y) * expf(pm - M);
+    }
+  }
+  const float S = wave_sum_f32(sum);
+  const float r = M == INFINITY ? INFINITY : M == -INFINITY ? -INFINITY : M + logf(S);
+  if (lane_id() == 0 && out != nullptr) *out = r;
+  return r;
+}
+// The row's pairs for lse_wave, requested by the waves with `mine` set
+// (n <= 64 * kLsePairs).
+__device__ __forceinline__ void load_lse_pairs_wave(const uint2* part, int n, bool mine,
+                                                    uint2 (&p)[kLsePairs]) {
+#pragma unroll
+  for (int j = 0; j < kLsePairs; ++j) {
+    const int i = lane_id() + j * 64;
+    p[j] = mine && i < n ? ld_cand(&part[i]) : make_uint2(__float_as_uint(-INFINITY), 0u);
+  }
+}
+
 __device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out, FinalSmem& fs,
                                           int mode, const uint2 (&pre)[kLsePairs],
                                           bool want = true) {
@@ -1519,8 +1551,12 @@ __device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out,
   const int lane = lane_id();
   const int wave = wave_id();
   const int nw = blockDim.x >> 6;
+  if (mode == 1) {
+    if (wave != 0) return 0.f;
+    const float r = lse_wave(pre, out);
+    return want ? r : 0.f;
+  }
   const bool have = mode != 0;
-  if (mode == 1 && wave != 0) return 0.f;
   // 1. the row's maximum M
   float mx = -INFINITY;
   if (have) {
@@ -1530,12 +1566,9 @@ __device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out,
     for (int i = tid; i < n; i += (int)blockDim.x) mx = fmaxf(mx, __uint_as_float(ld_cand(&part[i]).x));
   }
   mx = wave_max_f32(mx);
-  float M = mx;
-  if (mode != 1) {
-    if (lane == 0) fs.lse_w[wave].x = __float_as_uint(mx);
-    lds_barrier();
-    M = wave_max_f32(lane < nw ? __uint_as_float(fs.lse_w[lane].x) : -INFINITY);
-  }
+  if (lane == 0) fs.lse_w[wave].x = __float_as_uint(mx);
+  lds_barrier();
+  const float M = wave_max_f32(lane < nw ? __uint_as_float(fs.lse_w[lane].x) : -INFINITY);
   // 2. the sum of s * exp(m - M)
   float sum = 0.f;
   if (M != INFINITY && M != -INFINITY) {
@@ -1551,12 +1584,9 @@ __device__ __forceinline__ float merge_lse(const uint2* part, int n, float* out,
     }
   }
   sum = wave_sum_f32(sum);
-  float S = sum;
-  if (mode != 1) {
-    if (lane == 0) fs.lse_w[wave].y = __float_as_uint(sum);
-    lds_barrier();
-    S = wave_sum_f32(lane < nw ? __uint_as_float(fs.lse_w[lane].y) : 0.f);
-  }
+  if (lane == 0) fs.lse_w[wave].y = __float_as_uint(sum);
+  lds_barrier();
+  const float S = wave_sum_f32(lane < nw ? __uint_as_float(fs.lse_w[lane].y) : 0.f);
   const float r = M == INFINITY ? INFINITY : M == -INFINITY ? -INFINITY : M + logf(S);
   if (tid == 0 && out != nullptr) *out = r;
   return want ? r : 0.f;

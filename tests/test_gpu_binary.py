@@ -162,24 +162,47 @@ def test_full_int8_range_including_minus_128(M):
     c.check(50)
 
 
+@pytest.mark.parametrize("with_lse", [False, True])
 @pytest.mark.parametrize("M", [2, 5, 8])
-def test_rows_select_independently(M):
-    # The rows' small-k chunk selections share their barriers.  Row 1 has
-    # zero activations, so all its logits are equal: every chunk stages all
-    # of its rows, more than the small-k staging holds, and that row takes
-    # the radix select while the other rows keep the small-k one.  Each row
-    # equals the oracle and, bit for bit, its own result alone (M = 1).
-    H, V = 1024, 20000
+def test_rows_select_independently(M, with_lse):
+    # The rows' small-k chunk selections share their barriers, and with 50 to
+    # 256 chunks of 16 waves the rows' merges run side by side (one group of
+    # waves per row, each row's log-sum-exp by its group's first wave).  Row 1
+    # has zero activations, so all its logits are equal: every chunk stages
+    # all of its rows, more than the small-k staging holds, and that row takes
+    # the radix select while the other rows keep the small-k one; in the
+    # merge it has more survivors than its group holds and is merged by the
+    # whole workgroup afterwards.  Each row equals the oracle and, bit for
+    # bit, its own result alone (M = 1).
+    H, V, k = 1024, 32001, 50
+    _, n_chunks, waves = lt.binary_plan(M, V, H, k)
+    assert k <= n_chunks <= 256 and waves == 16, "sizes of the side-by-side merge"
     rng = np.random.default_rng(M)
     act_q = rng.integers(-128, 128, size=(M, H)).astype(np.int8)
     act_q[1, :] = 0
     act_scale = (rng.random(M).astype(np.float32) + 0.5) * np.float32(1e-2)
     c = Case(M, H, V, seed=11, act=(act_q, act_scale))
-    v, i, _ = c.check(50)
-    assert np.array_equal(i.cpu().numpy()[1], np.arange(50)), "equal logits: the lowest indices"
+
+    def call(rows):
+        aq, sc = c.d_act[rows].contiguous(), c.d_scale[rows].contiguous()
+        lse = torch.empty(len(rows), device="cuda") if with_lse else None
+        v, i = lt.lm_head_topk_binary(aq, sc, c.wq, c.ws, k=k, vocab_size=V, lse=lse)
+        torch.cuda.synchronize()
+        return v, i, lse
+
+    v, i, lse = call(list(range(M)))
+    eps = binary_eps_fn(c.act_q, c.act_scale, lambda ix: c.scales[ix], None, c.G)
+    compare_end_to_end(c.L, v.cpu().numpy(), i.cpu().numpy(), k, RTOL_BINARY, eps)
+    assert np.array_equal(i.cpu().numpy()[1], np.arange(k)), "equal logits: the lowest indices"
+    if with_lse:
+        want = oracle.logsumexp_rows(c.L)
+        tol = 1e-5 + 2.0**-22 * np.abs(want) + np.array([eps(m, np.arange(V)).max() for m in range(M)])
+        assert np.all(np.abs(lse.cpu().numpy() - want) <= tol)
     for m in (0, 1, M - 1):
-        v1, i1 = c.run(50, rows=[m])
+        v1, i1, l1 = call([m])
         assert torch.equal(i1[0], i[m]) and torch.equal(v1[0].view(torch.int32), v[m].view(torch.int32))
+        if with_lse:
+            assert torch.equal(l1.view(torch.int32)[0], lse.view(torch.int32)[m])
 
 
 # ---------------------------------------------------------------------------
