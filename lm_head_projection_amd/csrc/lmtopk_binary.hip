@@ -73,21 +73,41 @@ __device__ __forceinline__ void plane_dot(const uint4 (&w)[R], const uint4* pg, 
   }
 }
 
-// From four rows on (one row per lane): the sign bits of two words (64
-// elements) as 16 words of four 0/1 bytes, e[k] holding the bits of
-// elements 4k .. 4k + 3 of that half.  A nibble n is spread to the low bits
-// of four bytes by n * 0x204081 = n + (n << 7) + (n << 14) + (n << 21): the
-// four partial products occupy disjoint bits, and bit j of n lands on bit
-// 8j, the only bits the mask keeps.  The words are shared by all M rows; S
-// of a row is then one v_dot4_i32_i8 per four elements with the row's
-// activation bytes, the same exact integer as the plane sum, for 96 + 32 M
-// instructions per group against 64 M.
-__device__ __forceinline__ void spread_signs(uint32_t w0, uint32_t w1, uint32_t (&e)[16]) {
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    e[n] = (__builtin_amdgcn_ubfe(w0, 4 * n, 4) * 0x00204081u) & 0x01010101u;
-    e[8 + n] = (__builtin_amdgcn_ubfe(w1, 4 * n, 4) * 0x00204081u) & 0x01010101u;
-  }
+// From four rows on (one row per lane) a group's integer sums come from the
+// matrix cores.  For each block of 16 rows of the tile, two
+// v_mfma_i32_16x16x64_i8 (64 elements each) multiply the activation bytes
+// (A, 16 x 64: activation row m in lanes m, 16 + m, 32 + m, 48 + m; rows M
+// to 15 repeat row 0 and are not used) by the sign bits as 0/1 bytes (B,
+// 64 x 16: the block's rows) into 16 x 16 integer sums.  Lane layouts on
+// gfx950: lane 16 q + j holds elements [16 q, 16 q + 16) of A's row j and of
+// B's column j, and rows 4 q .. 4 q + 3 of column j of the sums.
+//   The sign bits arrive one row per lane (four words); transpose4 over the
+// four lane groups gives lane 16 q + p word q of the rows 16 b + p, b = 0..3,
+// and (y >> j) & 0x01010101, j = 0..7, spreads a word into bytes: byte i of
+// spread j is bit 8 i + j.  The activation bytes are kept in LDS in the
+// matching order (element 32 q + 8 i + j of a group at byte 32 q + 4 j + i,
+// act_byte_slot).  The same transpose brings each row's sums back to the
+// row's own lane.  The sums are the same exact integers as the bit-plane
+// sums: 4 + 60 + 12 + 3 M vector instructions and 8 matrix instructions
+// per group, against 96 + 32 M with 8-bit dot products.
+typedef int v4i32_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t kByteBits = 0x01010101u;
+__device__ __forceinline__ uint32_t act_byte_slot(uint32_t e) {
+  return (e & ~31u) | ((e & 7u) << 2) | ((e >> 3) & 3u);
+}
+// Register j of lane 16 q + p receives register q of lane 16 j + p (a 4 x 4
+// transpose of lane groups and registers): first the upper lane half of
+// r0 / r1 with the lower half of r2 / r3, then the odd lane groups of r0 /
+// r2 with the even ones of r1 / r3.
+__device__ __forceinline__ void transpose4(uint32_t& r0, uint32_t& r1, uint32_t& r2, uint32_t& r3) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(r0, r2, false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(r1, r3, false, false);
+  const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+  const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+  r0 = s01[0];
+  r1 = s01[1];
+  r2 = s23[0];
+  r3 = s23[1];
 }
 
 // Lane l of wave w owns the R rows ((chunk * tiles_per_chunk + w * R + r) * 64 + l),
@@ -159,8 +179,8 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   __shared__ uint32_t task_next;  // kTasks: the next task index to hand out
   HeadStage& hst = csm.hs;
   head_stage_init<(M >= 2)>(hst);  // ordered by the barriers below
-  // from four rows on, the activation bytes and 8-bit dot products (see
-  // spread_signs) take fewer instructions than the bit planes
+  // from four rows on, the activation bytes and the matrix cores (see
+  // transpose4) take fewer instructions than the bit planes
   constexpr bool kBytes = M >= 4 && R == 1;
   const int G = a.G;
   PlaneGroup* pgs = reinterpret_cast<PlaneGroup*>(dyn_lds);          // [M][G]
@@ -171,6 +191,7 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   const int lane = lane_id();
   const int wave = wave_id();
   const int nw = blockDim.x >> 6;
+  const int a_row = (lane & 15) < M ? (lane & 15) : 0;  // kBytes: this lane's activation row of A
   const int Qf = G >> 2;  // full quads
   const bool pair = R == 1 && a.ks == 2;
   const bool second = pair && (wave & 1);  // runs the second chain of a pair
@@ -230,10 +251,10 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
           mine = make_uint4((uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1, (uint32_t)(b1 >> 32));
         cgroup += (p == 7 ? -128 : 1 << p) * (__popcll(b0) + __popcll(b1));
       }
-      if constexpr (kBytes) {  // the activation bytes themselves
+      if constexpr (kBytes) {  // the activation bytes themselves, in matrix-core order
         uint8_t* slot = reinterpret_cast<uint8_t*>(&pgs[mg]);
-        slot[lane] = (uint8_t)a0;
-        slot[64 + lane] = (uint8_t)a1;
+        slot[act_byte_slot((uint32_t)lane)] = (uint8_t)a0;
+        slot[act_byte_slot(64u + (uint32_t)lane)] = (uint8_t)a1;
       } else {
         if (lane < 8) pgs[mg].plane[lane] = mine;
       }
@@ -334,30 +355,36 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
 
   auto compute_group = [&](int g, const uint4 (&w)[R], const float (&s)[R]) {
     if constexpr (kBytes) {
-      // two halves of 64 elements, so only 16 spread words are live at once
-      int sacc[M];
+      static_assert(M <= 8, "sums of rows 0-7 come back in two registers");
+      uint32_t y0 = w[0].x, y1 = w[0].y, y2 = w[0].z, y3 = w[0].w;
+      transpose4(y0, y1, y2, y3);  // y_b: word q of row 16 b + p
+      const uint8_t* ag = reinterpret_cast<const uint8_t*>(pgs + (size_t)a_row * G + g) + 32 * (lane >> 4);
+      const v4i32_t a0 = *reinterpret_cast<const v4i32_t*>(ag);
+      const v4i32_t a1 = *reinterpret_cast<const v4i32_t*>(ag + 16);
+      const v4i32_t zero = {0, 0, 0, 0};
+      v4i32_t c[4];
 #pragma unroll
-      for (int m = 0; m < M; ++m) sacc[m] = 0;
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t x = b == 0 ? y0 : b == 1 ? y1 : b == 2 ? y2 : y3;
+        const v4i32_t lo = {(int)(x & kByteBits), (int)((x >> 1) & kByteBits), (int)((x >> 2) & kByteBits),
+                            (int)((x >> 3) & kByteBits)};
+        const v4i32_t hi = {(int)((x >> 4) & kByteBits), (int)((x >> 5) & kByteBits),
+                            (int)((x >> 6) & kByteBits), (int)((x >> 7) & kByteBits)};
+        c[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, lo, zero, 0, 0, 0);
+        c[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, hi, c[b], 0, 0, 0);
+      }
+      // activation row 4 j + i of this lane's row: register j of the
+      // transpose of (c[0][i], .., c[3][i])
+      int d[8];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        uint32_t e[16];
-        spread_signs(half ? w[0].z : w[0].x, half ? w[0].w : w[0].y, e);
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const uint4* ab = pgs[(size_t)m * G + g].plane + 4 * half;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint4 av = ab[q];
-            sacc[m] = __builtin_amdgcn_sdot4((int)av.x, (int)e[4 * q], sacc[m], false);
-            sacc[m] = __builtin_amdgcn_sdot4((int)av.y, (int)e[4 * q + 1], sacc[m], false);
-            sacc[m] = __builtin_amdgcn_sdot4((int)av.z, (int)e[4 * q + 2], sacc[m], false);
-            sacc[m] = __builtin_amdgcn_sdot4((int)av.w, (int)e[4 * q + 3], sacc[m], false);
-          }
-        }
+      for (int i = 0; i < 4; ++i) {
+        uint32_t r0 = (uint32_t)c[0][i], r1 = (uint32_t)c[1][i], r2 = (uint32_t)c[2][i], r3 = (uint32_t)c[3][i];
+        transpose4(r0, r1, r2, r3);
+        d[i] = (int)r0;
+        d[4 + i] = (int)r1;
       }
 #pragma unroll
-      for (int m = 0; m < M; ++m)
-        acc[0][m] = fmaf((float)(2 * sacc[m] - cg[m * G + g]), s[0], acc[0][m]);
+      for (int m = 0; m < M; ++m) acc[0][m] = fmaf((float)(2 * d[m] - cg[m * G + g]), s[0], acc[0][m]);
     } else {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
