@@ -261,19 +261,7 @@ static void* const* score_events(const lmtopk_options* opt) {
 // gfx950's LDS (M and H are checked elsewhere; any value here is safe).
 static int binary_split_ok(int64_t M, int64_t H) {
   return H >= 1 && M >= 1 && M <= LMTOPK_MAX_ROWS && H <= LMTOPK_MAX_BINARY_MH &&
-         lmtopk::binary_lds_bytes(M, H, 2, 0, 1) + lmtopk::kChunkStaticLds <= lmtopk::kLdsPerBlock;
-}
-
-// With four to six rows the binary path shares the tiles' second group
-// chains out as tasks among the waves (one wave per tile, one row per lane) where
-// every chain has at least two full quads and the chain sums fit the LDS.
-static void binary_tasks(Geometry* g, int64_t H) {
-  const int64_t G = H / LMTOPK_GROUP_SIZE;
-  g->tasks = g->ks == 1 && g->rpl == 1 && g->M >= lmtopk::kMinRowsTasks &&
-             g->M <= lmtopk::kMaxRowsTasks && G % 4 == 0 &&
-             G / 4 >= 4 &&
-             lmtopk::binary_lds_bytes(g->M, H, 1, 1, 1) + lmtopk::kChunkStaticLds <=
-                 lmtopk::kLdsPerBlock;
+         lmtopk::binary_lds_bytes(M, H, 2, 1) + lmtopk::kChunkStaticLds <= lmtopk::kLdsPerBlock;
 }
 
 lmtopk_status lmtopk_binary_plan(int64_t M, int64_t V, int64_t H, int32_t k,
@@ -309,13 +297,12 @@ static lmtopk_status binary_checks(const int8_t* act_q, const float* act_scale, 
   if (group_size != LMTOPK_GROUP_SIZE || H % LMTOPK_GROUP_SIZE != 0) return LMTOPK_ERR_GROUP;
   if (M * H > LMTOPK_MAX_BINARY_MH) return LMTOPK_ERR_SHAPE;
   if (g->rpl > 1 && M > lmtopk::kMaxRowsWide) return LMTOPK_ERR_OPTIONS;
-  binary_tasks(g, H);
   if (!lmtopk::aligned16(act_q) || !lmtopk::aligned16(act_scale) || !lmtopk::aligned16(wq) ||
       !lmtopk::aligned16(wscale) || (bias && !lmtopk::aligned16(bias)))
     return LMTOPK_ERR_ALIGN;
   size_t lds_max = 0;
   if (lmtopk::max_lds_per_block(&lds_max)) return LMTOPK_ERR_HIP;
-  if (lmtopk::binary_lds_bytes(M, H, g->ks, g->tasks, g->rpl) + lmtopk::kChunkStaticLds > lds_max)
+  if (lmtopk::binary_lds_bytes(M, H, g->ks, g->rpl) + lmtopk::kChunkStaticLds > lds_max)
     return LMTOPK_ERR_SHAPE;
   return LMTOPK_OK;
 }

@@ -73,7 +73,7 @@ __device__ __forceinline__ void plane_dot(const uint4 (&w)[R], const uint4* pg, 
   }
 }
 
-// From four rows on (one row per lane) a group's integer sums come from the
+// From two rows on (one row per lane) a group's integer sums come from the
 // matrix cores.  For each block of 16 rows of the tile, two
 // v_mfma_i32_16x16x64_i8 (64 elements each) multiply the activation bytes
 // (A, 16 x 64: activation row m in lanes m, 16 + m, 32 + m, 48 + m; rows M
@@ -156,37 +156,21 @@ __device__ __forceinline__ float4 as_float4(u32x4_t v) {
 // kExtras: a log-sum-exp output or a bitmask; kSample (implies kExtras): a
 // token draw.  Calls without them run instances with that code left out.
 //
-// kTasks (four to six rows, one row per lane, one wave per tile, G % 4 ==
-// 0, Q >= 4): the second chains of the tiles are tasks shared by the
-// workgroup's waves.  There the scorer is bound by each wave's VALU work,
-// and the waves a SIMD favours finish well before the others; here wave w
-// runs the first chain of tile w (issued in the prologue as usual, its sums
-// kept in registers) and then takes second chains from an LDS counter as it
-// runs out of work, so the favoured waves take more of them.  A finished
-// second chain's sums go to LDS; after a barrier wave w adds the two chains
-// of tile w (first + second) and selects as before.  Every chain is
-// computed by one wave in the fixed order, so the results are those of the
-// other paths.  (With fewer rows the head's streaming dominates and the
-// fixed assignment with its overlapped selection measured faster, and with
-// seven and eight rows too.)
-template <int M, int R, bool kExtras, bool kSample = false, bool kTasks = false>
+template <int M, int R, bool kExtras, bool kSample = false>
 __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs a) {
-  static_assert(!kTasks || (R == 1 && M >= kMinRowsTasks), "chain tasks: one row per lane, M >= 4");
   extern __shared__ __align__(16) uint8_t dyn_lds[];
   __shared__ SelectSmem ssm;
   __shared__ ChunkSmem csm;
   __shared__ uint32_t last_wg;
-  __shared__ uint32_t task_next;  // kTasks: the next task index to hand out
   HeadStage& hst = csm.hs;
   head_stage_init<(M >= 2)>(hst);  // ordered by the barriers below
-  // from four rows on, the activation bytes and the matrix cores (see
-  // transpose4) take fewer instructions than the bit planes
-  constexpr bool kBytes = M >= 4 && R == 1;
+  // from two rows on (one row per lane), the activation bytes and the
+  // matrix cores (see transpose4) take fewer instructions than the bit planes
+  constexpr bool kBytes = M >= 2 && R == 1;
   const int G = a.G;
   PlaneGroup* pgs = reinterpret_cast<PlaneGroup*>(dyn_lds);          // [M][G]
   int* cg = reinterpret_cast<int*>(pgs + (size_t)M * G);              // [M][G] C of the group
   float* xch = reinterpret_cast<float*>(cg + (size_t)M * G);          // ks = 2: [waves][32][M]
-  float* tpart = xch;  // kTasks: second-chain sums [tile][M][64]
   uint32_t* xflag = reinterpret_cast<uint32_t*>(xch + (size_t)kPairWaves * 32 * M);  // [waves]
   const int lane = lane_id();
   const int wave = wave_id();
@@ -205,7 +189,6 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   const int qb = pair && !second ? Qh : a.Q;
   const int split = pair ? -1 : Qh;
   if (pair && threadIdx.x < kPairWaves) xflag[threadIdx.x] = 0u;  // ordered by the barrier below
-  if (kTasks && threadIdx.x == 0) task_next = (uint32_t)nw;  // the second chains come after
 
   // a tile past the last one reads the last tile; its rows are never offered
   const uint4* wp[R];
@@ -339,7 +322,7 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   // that chain's sums in LDS until the second chain is done, instead of in
   // registers the main loop needs (at eight rows they cost 5 % in time);
   // slot (wave * R + r, m) of this lane.
-  float* park = xch + (kTasks ? (size_t)kPairWaves * M * 64 : 0) + (size_t)wave * R * M * 64 + lane;
+  float* park = xch + (size_t)wave * R * M * 64 + lane;
   auto park_chain = [&]() {
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -418,111 +401,7 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
     }
   };
 
-  if constexpr (kTasks) {
-    // Task t < T: first chain (quads [0, Qh)) of tile t; t >= T: second chain
-    // (quads [Qh, Q)) of tile t - T.  Each wave streams a sequence of
-    // (task, quad) elements through the two buffers; bt / bq say what each
-    // buffer holds (-1: the sequence has ended), (lt, lq) is the element
-    // loaded last (lt -1: no task left).
-    const int T = nw;
-    const int64_t tile_base = (int64_t)blockIdx.x * a.tiles_per_chunk;
-    auto grab = [&]() -> int {  // the next second chain whose tile exists
-      for (;;) {  // the counter only grows: at most 2 T rounds
-        uint32_t j = 0u;
-        if (lane == 0) j = atomicAdd(&task_next, 1u);
-        const int t = (int)uniform(j);
-        if (t >= 2 * T) return -1;
-        if (tile_base + (t - T) < a.n_tiles) return t;
-      }
-    };
-    // The element loaded last: task lt (-1: none left), quad lq, and the end
-    // quad of that task; rw / rs address the task's tile (sign bits and
-    // scales).  They change only when a wave moves to a new task.
-    auto tile_rsrc = [&](int t, __amdgpu_buffer_rsrc_t& rw, __amdgpu_buffer_rsrc_t& rs) {
-      const bool real = t >= 0;
-      const size_t tg = (size_t)(tile_base + (!real ? 0 : t < T ? t : t - T));
-      rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(a.wq + tg * G * 64), (short)0,
-                                             real ? G * 1024 : 0, kRsrcWord3);
-      rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float4*>(a.wscale + tg * a.Q * 64),
-                                             (short)0, real ? a.Q * 1024 : 0, kRsrcWord3);
-    };
-    int lt = active ? wave : -1, lq = 1, lend = Qh;
-    __amdgpu_buffer_rsrc_t rw, rs;
-    tile_rsrc(lt, rw, rs);
-    auto next_elem = [&]() {
-      if (lt < 0) return;
-      if (++lq == lend) {
-        lt = grab();
-        lq = lt >= 0 ? Qh : 0;
-        lend = a.Q;
-        tile_rsrc(lt, rw, rs);
-      }
-    };
-    // Loads element (lt, lq) into a buffer.  With no element left (lt < 0)
-    // the loads are still issued, against an empty buffer range, which reads
-    // no memory and returns zeros: every path through the loop then issues
-    // the same loads, so each wait covers only the buffer about to be used.
-    const int lane16 = lane * 16;
-    auto load_elem = [&](uint4 (&w)[R][4], float4 (&sc)[R]) {
-      sc[0] = as_float4(__builtin_amdgcn_raw_buffer_load_b128(rs, lane16 + lq * 1024, 0, kBufNt));
-      const int vo = lane16 + lq * 4096;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[0][i] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rw, vo + i * 1024, 0, kBufNt));
-    };
-    // what each buffer holds: task (-1: nothing), quad, and whether that
-    // quad completes its chain
-    int bt[kQuadBuffers], bq[kQuadBuffers];
-    bool bl[kQuadBuffers];
-#pragma unroll
-    for (int b = 0; b < kQuadBuffers; ++b) {
-      bt[b] = active ? wave : -1;  // the prologue loaded quads 0 and 1 of tile `wave`
-      bq[b] = b;
-      bl[b] = b + 1 == Qh;
-    }
-    // (a wave without a tile of its own, in the last chunk, takes no task)
-    // computes the element in buffer b, if it holds one (a chain's last quad
-    // stores its sums), then refills the buffer with the next element (or
-    // the empty-range load when none is left)
-    auto step = [&](int b) {
-      if (bt[b] >= 0) {
-        compute_quad(bq[b], buf[b], sbuf[b]);
-        if (bl[b]) {  // a chain is complete: its own first chain is parked
-          if (bt[b] < T) {
-            park_chain();
-          } else {
-            float* dst = tpart + (size_t)(bt[b] - T) * M * 64 + lane;
-#pragma unroll
-            for (int m = 0; m < M; ++m) {
-              dst[m * 64] = acc[0][m];
-              acc[0][m] = 0.f;
-            }
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      next_elem();
-      bt[b] = lt;
-      bq[b] = lq;
-      bl[b] = lq + 1 == lend;
-      load_elem(buf[b], sbuf[b]);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // The buffers hold consecutive elements, so buffer 1 is empty once
-    // buffer 0 is; every pass of the loop issues both refills.
-    if (active) {
-      do {
-        step(0);
-        step(1);
-      } while (bt[0] >= 0);
-    }
-    lds_barrier();  // every second chain's sums are in LDS
-    if (active) {
-      const float* p1 = tpart + (size_t)wave * M * 64 + lane;
-#pragma unroll
-      for (int m = 0; m < M; ++m) acc[0][m] = p1[m * 64];
-    }
-  } else if (active) {
+  if (active) {
     // quads q .. q + kQuadBuffers - 1 are in flight at the top; each buffer is
     // refilled right after its last use
     constexpr int NB = kQuadBuffers;
@@ -652,12 +531,12 @@ namespace {
 
 // mode 0: plain; 1: log-sum-exp output or bitmask; 2: also a token draw
 // (kernels without them leave that code out)
-template <int M, int R, bool kTasks = false>
+template <int M, int R>
 void (*binary_kernel_mr(int mode))(BinaryArgs) {
   switch (mode) {
-    case 0: return k_binary_chunk<M, R, false, false, kTasks>;
-    case 1: return k_binary_chunk<M, R, true, false, kTasks>;
-    case 2: return k_binary_chunk<M, R, true, true, kTasks>;
+    case 0: return k_binary_chunk<M, R, false, false>;
+    case 1: return k_binary_chunk<M, R, true, false>;
+    case 2: return k_binary_chunk<M, R, true, true>;
   }
   return nullptr;
 }
@@ -665,11 +544,7 @@ void (*binary_kernel_mr(int mode))(BinaryArgs) {
 // three rows on their accumulators and weight buffers no longer fit the
 // registers (the host refuses that option there).
 template <int M>
-void (*binary_kernel_m(int rpl, int mode, bool tasks))(BinaryArgs) {
-  if constexpr (M >= kMinRowsTasks && M <= kMaxRowsTasks) {
-    if (tasks) return rpl == 1 ? binary_kernel_mr<M, 1, true>(mode) : nullptr;
-  }
-  if (tasks) return nullptr;
+void (*binary_kernel_m(int rpl, int mode))(BinaryArgs) {
   if (rpl == 1) return binary_kernel_mr<M, 1>(mode);
   if constexpr (M <= kMaxRowsWide) {
     if (rpl == 4) return binary_kernel_mr<M, 4>(mode);
@@ -677,29 +552,28 @@ void (*binary_kernel_m(int rpl, int mode, bool tasks))(BinaryArgs) {
   return nullptr;
 }
 
-void (*binary_kernel(int M, int rpl, int mode, bool tasks))(BinaryArgs) {
+void (*binary_kernel(int M, int rpl, int mode))(BinaryArgs) {
   switch (M) {
-    case 1: return binary_kernel_m<1>(rpl, mode, tasks);
-    case 2: return binary_kernel_m<2>(rpl, mode, tasks);
-    case 3: return binary_kernel_m<3>(rpl, mode, tasks);
-    case 4: return binary_kernel_m<4>(rpl, mode, tasks);
-    case 5: return binary_kernel_m<5>(rpl, mode, tasks);
-    case 6: return binary_kernel_m<6>(rpl, mode, tasks);
-    case 7: return binary_kernel_m<7>(rpl, mode, tasks);
-    case 8: return binary_kernel_m<8>(rpl, mode, tasks);
+    case 1: return binary_kernel_m<1>(rpl, mode);
+    case 2: return binary_kernel_m<2>(rpl, mode);
+    case 3: return binary_kernel_m<3>(rpl, mode);
+    case 4: return binary_kernel_m<4>(rpl, mode);
+    case 5: return binary_kernel_m<5>(rpl, mode);
+    case 6: return binary_kernel_m<6>(rpl, mode);
+    case 7: return binary_kernel_m<7>(rpl, mode);
+    case 8: return binary_kernel_m<8>(rpl, mode);
   }
   return nullptr;
 }
 }  // namespace
 
-size_t binary_lds_bytes(int64_t M, int64_t H, int ks, int tasks, int rpl) {
+size_t binary_lds_bytes(int64_t M, int64_t H, int ks, int rpl) {
   const int64_t G = H / kGroup;
   const int64_t pair = (int64_t)kPairWaves * (32 * M * 4 + 4);
-  const int64_t chains = tasks ? (int64_t)kPairWaves * M * 64 * 4 : 0;  // <= 16 tiles
   // parked first chains: one per wave and row of a lane (16 waves of one
   // row, or 8 waves of four)
   const int64_t parked = (int64_t)(rpl == 1 ? 16 : 32) * M * 64 * 4;
-  return (size_t)(M * G * sizeof(PlaneGroup) + M * G * 4 + (ks == 2 ? pair : chains + parked));
+  return (size_t)(M * G * sizeof(PlaneGroup) + M * G * 4 + (ks == 2 ? pair : parked));
 }
 int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* act_scale,
                          const void* wq, const float* wscale, const float* bias, int64_t H,
@@ -720,9 +594,9 @@ int launch_binary_chunks(const Geometry& g, const int8_t* act_q, const float* ac
   a.ks = g.ks;
   a.out = chunk_out(g, workspace, values, indices);
   const int mode = g.smp.on ? 2 : (g.lse != nullptr || g.allowed != nullptr) ? 1 : 0;
-  auto kern = binary_kernel((int)g.M, g.rpl, mode, g.tasks != 0);
+  auto kern = binary_kernel((int)g.M, g.rpl, mode);
   if (!kern) return (int)hipErrorInvalidValue;
   return (int)launch1(kern, dim3(g.n_chunks), dim3(64 * g.nw),
-                      binary_lds_bytes(g.M, H, g.ks, g.tasks, g.rpl), stream, a, events);
+                      binary_lds_bytes(g.M, H, g.ks, g.rpl), stream, a, events);
 }
 }  // namespace lmtopk

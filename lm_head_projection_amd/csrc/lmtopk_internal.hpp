@@ -68,8 +68,6 @@ struct Geometry {
   int ks;          // waves per 64-row tile: 1, or 2 (binary path: each wave
                    // scores half of the groups); C * ks = 64 * nw * rpl
   int nw;          // waves per chunk workgroup
-  int tasks;       // binary path: the tiles' group chains are shared out as
-                   // tasks among the waves (one row per lane, ks = 1)
   int n_chunks;
   int kc;          // candidate slots per chunk per row = min(k, C)
   int64_t n_tiles; // 64-row tiles covering V
@@ -135,13 +133,8 @@ constexpr size_t kChunkStaticLds = 57344;
 // it does not need a device; the launch checks the device's own limit).
 constexpr size_t kLdsPerBlock = 163840;
 
-// LDS bytes the scoring kernels need; ks = waves per tile, tasks: chain
-// tasks, rpl: rows per lane.
-size_t binary_lds_bytes(int64_t M, int64_t H, int ks, int tasks, int rpl);
-// Chain tasks (Geometry::tasks) serve this range of activation rows (with
-// seven and eight rows the fixed assignment measured faster).
-constexpr int kMinRowsTasks = 4;
-constexpr int kMaxRowsTasks = 6;
+// LDS bytes the scoring kernels need; ks = waves per tile, rpl: rows per lane.
+size_t binary_lds_bytes(int64_t M, int64_t H, int ks, int rpl);
 size_t dense_lds_bytes(int64_t M, int chunk_rows);
 
 }  // namespace lmtopk

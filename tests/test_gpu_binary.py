@@ -327,9 +327,9 @@ def test_cfg5_sweep_with_bias(flagship, M, k):
 # ---------------------------------------------------------------------------
 # chunk sizes x optional outputs: every binary kernel instance that exists
 # runs (2048-row chunks, four rows per lane, serve M <= 2; from three rows on
-# the library refuses them), with one wave per tile (1,024 and 2,048 rows;
-# at 1,024 rows and M = 4 the tiles' second chains are shared out as tasks) and
-# with two (up to 512 rows; the automatic size at V = 20,001)
+# the library refuses them), with one wave per tile (1,024 and 2,048 rows)
+# and with two (up to 512 rows; the automatic size at V = 20,001); from two
+# rows on, with one row per lane, the group sums come from the matrix cores
 # ---------------------------------------------------------------------------
 @pytest.fixture(scope="module")
 def wide_case():
@@ -378,9 +378,8 @@ def test_chunk_sizes_and_extras(wide_case, M, chunk_rows, extras):
 # the two accumulation chains (quads [0, Qh) and [Qh, Q), Qh = floor(Q / 2)):
 # one wave running both (1,024 and 2,048-row chunks) and two waves sharing a
 # tile (512 and 64-row chunks) give the same bits for every group count,
-# including an empty first chain (G <= 3) and a partial last quad; from
-# G = 16 on (four quads per chain and G % 4 == 0) 1,024-row chunks with
-# four to six rows share the second chains out as tasks
+# including an empty first chain (G <= 3) and a partial last quad, with the
+# bit planes (one row, or four rows per lane) and with the matrix cores
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 7, 8, 9, 12, 13, 16, 20, 24])
 @pytest.mark.parametrize("M", [1, 2, 5])
@@ -420,11 +419,10 @@ def test_logits_follow_the_documented_fp32_order(M, G, C):
 
 @pytest.mark.parametrize("V", [3072 + 50, 1024 + 64, 4 * 1024, 2000])
 @pytest.mark.parametrize("M", [1, 4, 6])
-def test_chain_tasks_ragged_last_chunk(M, V):
-    """1,024-row chunks whose last chunk has from one tile up to all 16: with
-    four to six rows the waves without a tile of their own take no task,
-    the others take every second chain of the tiles that exist (one row:
-    the fixed assignment)."""
+def test_ragged_last_chunk_one_wave_per_tile(M, V):
+    """1,024-row chunks whose last chunk has from one tile up to all 16 (the
+    waves without a tile of their own score none): the same bits as
+    512-row chunks with two waves per tile."""
     c = Case(M, 2048, V, seed=V, with_bias=True)
     v0, i0, _ = c.check(40, chunk_rows=1024)
     v, i = c.run(40, chunk_rows=512)

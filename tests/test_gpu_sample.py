@@ -206,7 +206,7 @@ def test_lse_output_is_the_sampled_normaliser():
 
 @pytest.mark.parametrize("path,M,H,chunk_rows", [
     ("binary", 3, 1024, 0),
-    # five rows, 1,024-row chunks, G = 16: the second chains run as tasks
+    # five rows, 1,024-row chunks, G = 16: one wave per tile, matrix-core sums
     ("binary", 5, 2048, 1024),
     ("dense", 3, 1024, 0),
 ])
