@@ -468,7 +468,9 @@ __device__ __forceinline__ void head_stage_init(HeadStage& st) {
 // Counting over n entries in LDS, for each entry i < n:
 //   kAhead: rank[i] += #{j : key[j] > key[i], or key[j] == key[i] and
 //           idx[j] < idx[i]} (idx == nullptr: positions instead of idx), the
-//           entry's position in (key desc, idx asc) order;
+//           entry's position in (key desc, idx asc) order; idx >= 0, so
+//           (key, idx) compares as one unsigned 64-bit word, the key high
+//           and the complemented index low;
 //   else:   rank[i] += #{j : key[j] >= key[i]} (idx unused; the entry itself
 //           counts).
 // The jobs (slice of 16 entries j, read as four LDS broadcasts per array;
@@ -519,9 +521,11 @@ __device__ __forceinline__ void rank_count(const uint32_t* key, const int32_t* i
     const uint32_t ki = vi ? key[i] : 0u;
     const int32_t ii = (kAhead && vi) ? (idx ? idx[i] : (int32_t)i) : 0;
     uint32_t c = 0u;
+    const uint64_t ki64 = ((uint64_t)ki << 32) | (uint64_t)(~(uint32_t)ii);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const bool hit = kAhead ? (kj[e] > ki || (kj[e] == ki && ij[e] < ii)) : kj[e] >= ki;
+      const uint64_t kj64 = ((uint64_t)kj[e] << 32) | (uint64_t)(~(uint32_t)ij[e]);
+      const bool hit = kAhead ? kj64 > ki64 : kj[e] >= ki;
       c += ((uint32_t)e < m && hit) ? 1u : 0u;
     }
     if (vi && c) atomicAdd(&rank[i], c);
@@ -853,24 +857,35 @@ __device__ void select_top_rows(const uint32_t (&key)[M][R], uint32_t valid,
   }
   lds_barrier();
 
-  // 3. rank every row's staged rows, then emit each row's first k
+  // 3. rank every row's staged rows, then emit each row's first k; the
+  //    rows' ranking jobs, and then their entries, are dealt out to the
+  //    waves (threads) as one sequence, so no wave idles while others take
+  //    a job of every row
+  const uint32_t nw = blockDim.x >> 6;
   uint32_t n[M];
+  uint32_t jobs = 0u;  // ranking jobs of the rows before
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     n[m] = uniform(st.rcount[m]);
     const uint32_t o = (uint32_t)m * kSmallSurvivorsMax;
-    if (n[m] <= kSmallSurvivorsMax) rank_count(st.key + o, st.idx + o, n[m], st.rank + o);
+    if (n[m] <= kSmallSurvivorsMax && n[m] != 0u) {
+      rank_count(st.key + o, st.idx + o, n[m], st.rank + o, ((uint32_t)wave + nw - jobs % nw) % nw, nw);
+      jobs += ((n[m] + 15u) >> 4) * ((n[m] + 63u) >> 6);
+    }
   }
   lds_barrier();
+  uint32_t items = 0u;  // entries of the rows before
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const uint32_t o = (uint32_t)m * kSmallSurvivorsMax;
     if (n[m] <= kSmallSurvivorsMax) {
-      for (uint32_t i = tid; i < n[m]; i += blockDim.x) {
+      for (uint32_t i = ((uint32_t)tid + blockDim.x - items % blockDim.x) % blockDim.x; i < n[m];
+           i += blockDim.x) {
         const uint32_t r = st.rank[o + i];
         if (r < k) out(m, r, st.bits[o + i], st.idx[o + i]);
         st.rank[o + i] = 0u;
       }
+      items += n[m];
       n_out[m] = n[m] < k ? n[m] : k;
     } else {
       n_out[m] = 0xFFFFFFFFu;
