@@ -746,7 +746,8 @@ __device__ uint32_t select_top_small(const uint32_t (&key)[R], uint32_t valid,
 }
 
 // select_top_small for rows 0 .. M-1 of a chunk at once (the same P and h
-// for every row): the providers take their tops of every row in turn, the
+// for every row; from six rows on at most eight providers, with h raised to
+// keep P * h >= k): the providers take their tops of every row in turn, the
 // last provider of a row publishes its T, and every wave then stages each
 // row's keys >= T into that row's own part of the staging, so no row waits
 // for another row's barriers; the staged rows of all rows are ranked
@@ -767,6 +768,13 @@ __device__ void select_top_rows(const uint32_t (&key)[M][R], uint32_t valid,
   const int wave = wave_id();
   P = uniform(P);
   h = uniform(h);
+  // From six rows on the later providers' tops of every row come after the
+  // youngest waves have streamed; the first eight waves alone (still
+  // P * h >= k tops, at most 64) have theirs ready by then
+  if (M >= 6 && P > 8) {
+    P = 8;
+    h = ((int)k + 7) / 8;
+  }
   const bool stage_all = P == 0;
 
   // 1. providers: this wave's h largest keys of each row
