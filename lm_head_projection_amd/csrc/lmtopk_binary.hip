@@ -205,7 +205,8 @@ __global__ __launch_bounds__(R == 1 ? 1024 : 512) void k_binary_chunk(BinaryArgs
   // straight-line code, so the waits after it cover exactly what they need.
   // 1. bit planes of a batch of groups: each plane word is one ballot over
   //    64 activations (groups b0, b0 + nw, ..., this wave's share); from
-  //    four rows on the group's activation bytes themselves (kBytes)
+  //    two rows on (one row per lane) the group's activation bytes
+  //    themselves, in matrix-core order (kBytes)
   constexpr int kBatch = 4;
   const int n_mg = M * G;
   auto load_acts = [&](int b0, int8_t (&y0)[kBatch], int8_t (&y1)[kBatch]) {

@@ -142,7 +142,7 @@ def test_pack_signed_zero_and_golden_layout():
     (1, 128, 1, 1, False), (1, 128, 40, 40, True), (2, 640, 65, 7, False),
     (3, 512, 1000, 100, True), (8, 2048, 8192, 1, False), (8, 8192, 3000, 64, True),
     (4, 1024, 32001, 50, True), (1, 384, 70000, 2048, False),
-    # from four rows on the scorer uses activation bytes and 8-bit dot products
+    # from two rows on (one row per lane) the group sums come from the matrix cores
     (5, 1280, 5000, 50, False), (6, 384, 2049, 13, True), (7, 2560, 9000, 300, False),
 ])
 def test_binary_shapes(M, H, V, k, with_bias):
